@@ -1,0 +1,162 @@
+/*
+ * himuon.h - C ABI of the MI355X (gfx950) tiled Newton-Schulz library.
+ *
+ * What the library computes
+ * -------------------------
+ * HiMuon ("Hierarchical Muon: Tiled Newton-Schulz Updates for Efficient Muon
+ * Optimization", arXiv 2606.27216, abstract): every H x W momentum matrix is
+ * cut into T x T tiles anchored at (0, 0) (the last tile row and column hold
+ * the remainder, processed at their own h x w size), the same finite
+ * Newton-Schulz map is applied to every tile independently, and the results
+ * are written back in place.
+ *
+ * The per-tile map is Algorithm 1 of the "Gram Newton-Schulz" summary page
+ * (section 3, standard Newton-Schulz): X = Y / (||Y||_F + eps), then for
+ * t = 1..K:  A = X X^T,  B = b_t A + c_t A^2,  X = a_t X + B X.
+ * (The page's transpose of tall blocks only changes the cost: each step is an
+ * odd matrix polynomial, so the result is the same either way.)
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Matrices are row-major in device memory: element (i, j) of a descriptor
+ *   sits at ptr + i * ld + j (in elements).  rows >= 1, cols >= 1, ld >= cols.
+ *   All matrices of one call share one dtype.  Pointers must be aligned to the
+ *   element size; no other alignment is required (16-byte aligned rows take a
+ *   vector fast path).
+ * - The caller owns all device memory.  The library allocates no device memory
+ *   and keeps no device state between calls.  The descriptor array and the
+ *   coefficient array are read during the call only.
+ * - Work is enqueued on `stream` (a hipStream_t; NULL is the null stream) and
+ *   the call returns without waiting.  Results are valid once the stream has
+ *   reached that point.  The workspace must stay allocated until then.
+ * - Validation is all-or-nothing: when a call returns anything but HIMUON_OK,
+ *   nothing was enqueued and no memory was touched (HIMUON_ERR_HIP excepted: it
+ *   reports a launch failure from the HIP runtime; himuon_last_hip_error()
+ *   returns the hipError_t).
+ * - Matrices of one call must not overlap in memory (they are written in
+ *   place).  No exception crosses this interface.
+ * - Non-finite inputs are not an error: a NaN or Inf stays inside its tile.
+ * - Tile sizes T <= 128 with bf16 run one kernel launch per group of up to 64
+ *   matrices with every tile resident on chip for all K steps and need no
+ *   workspace.  Larger T, fp32 data, and T >= max(rows, cols) (the full-matrix
+ *   map) run step by step through the caller's workspace, in chunks of tiles
+ *   that each fit in `workspace_bytes`.
+ */
+#ifndef HIMUON_H
+#define HIMUON_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Largest K accepted by any entry point. */
+#define HIMUON_MAX_STEPS 16
+
+/* One matrix: device pointer to element (0, 0), its size and row stride. */
+typedef struct himuon_matrix {
+    void*   ptr;   /* device pointer, aligned to the element size           */
+    int64_t rows;  /* H >= 1                                                 */
+    int64_t cols;  /* W >= 1                                                 */
+    int64_t ld;    /* row stride in elements, ld >= cols                     */
+} himuon_matrix_t;
+
+typedef enum himuon_dtype {
+    HIMUON_BF16 = 0,   /* bfloat16 storage; bf16 MFMA with fp32 accumulation  */
+    HIMUON_FP32 = 1    /* float32 storage; fp32 arithmetic throughout         */
+} himuon_dtype_t;
+
+typedef enum himuon_status {
+    HIMUON_OK = 0,
+    HIMUON_ERR_INVALID_ARGUMENT = 1, /* null pointer, size < 1, ld < cols, K or eps out of range, non-finite coefficient */
+    HIMUON_ERR_UNSUPPORTED = 2,      /* dtype or option this build does not provide                                   */
+    HIMUON_ERR_LAYOUT = 3,           /* pointer not aligned to the element size, or an index that overflows int64   */
+    HIMUON_ERR_OVERLAP = 4,          /* two matrices that are written share memory                                  */
+    HIMUON_ERR_WORKSPACE = 5,        /* workspace too small for one tile of the step-by-step path, or NULL with bytes > 0 */
+    HIMUON_ERR_HIP = 6               /* the HIP runtime refused a launch                                            */
+} himuon_status_t;
+
+/* Summary of how a call would be carried out (host-side planning only). */
+typedef struct himuon_plan_info {
+    int64_t tiles;            /* tiles over all matrices                              */
+    int64_t resident_launches;/* launches of the on-chip kernel (T <= 128, bf16)      */
+    int64_t chunks;           /* chunks of the step-by-step path (0 if not used)      */
+    int64_t launches;         /* total kernel launches one call enqueues              */
+    int64_t kernel_tile;      /* on-chip kernel size (32, 64 or 128), or 0            */
+    size_t  workspace_full;   /* bytes the step-by-step path needs for one chunk      */
+    size_t  workspace_min;    /* bytes it needs for its largest single tile           */
+} himuon_plan_info_t;
+
+/*
+ * himuon_plan - describe how himuon_tiled_ns(m, n, T, K, ..., dt, ...,
+ * workspace_bytes) would run, without touching the GPU.  workspace_bytes is
+ * the cap the chunking must respect (ignored when no workspace is needed).
+ * Returns the same validation status the call would return (pointers are not
+ * dereferenced).
+ */
+himuon_status_t himuon_plan(const himuon_matrix_t* m, int32_t n, int32_t T, int32_t K,
+                            himuon_dtype_t dt, size_t workspace_bytes,
+                            himuon_plan_info_t* info);
+
+/*
+ * himuon_workspace_size - bytes of device workspace himuon_tiled_ns needs to
+ * run all tiles of these matrices in a single chunk (*full) and the least it
+ * accepts (*min, one tile).  Both are 0 when the call needs no workspace.
+ * Either output pointer may be NULL.
+ */
+himuon_status_t himuon_workspace_size(const himuon_matrix_t* m, int32_t n, int32_t T,
+                                      himuon_dtype_t dt, size_t* full, size_t* min);
+
+/*
+ * himuon_tiled_ns - HiMuon tiled Newton-Schulz, in place, on n matrices.
+ *
+ * m, n       : n >= 0 matrix descriptors (n == 0 is a no-op).
+ * T          : tile edge, T >= 1.  Tiles are T x T anchored at (0, 0); edge
+ *              tiles are h x w with h, w <= T.  T >= max(rows, cols) gives the
+ *              full-matrix Newton-Schulz map of each matrix.
+ * K          : number of Newton-Schulz steps, 0 <= K <= HIMUON_MAX_STEPS
+ *              (K = 0 writes the Frobenius-normalised tiles).
+ * abc        : 3*K floats, step t uses (a_t, b_t, c_t) = abc[3t .. 3t+2];
+ *              may be NULL when K == 0.  Must be finite.
+ * dt         : storage dtype of every matrix.
+ * eps        : added to each tile's Frobenius norm (>= 0, finite); 1e-7 in
+ *              the page's Algorithm 1.
+ * workspace, workspace_bytes : device scratch for the step-by-step path; the
+ *              tiles are processed in chunks that fit.  May be NULL / 0 when
+ *              himuon_workspace_size reports 0.
+ * stream     : hipStream_t to enqueue on.
+ */
+himuon_status_t himuon_tiled_ns(const himuon_matrix_t* m, int32_t n, int32_t T, int32_t K,
+                                const float* abc, himuon_dtype_t dt, float eps,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * himuon_muon_step - fused Muon update with the tiled map in place of polar()
+ * ("Gram Newton-Schulz" summary page, section 3, the Muon update rule):
+ *     M <- mu M + G            (stored back into M, rounded to dt)
+ *     W <- W - eta * tiledNS(M)
+ * W[i], M[i], G[i] must have equal rows and cols (their ld may differ).  W and
+ * M are written; G is read only.  No W, M or G may overlap any written matrix.
+ * Other arguments as for himuon_tiled_ns; mu and eta must be finite.
+ */
+himuon_status_t himuon_muon_step(const himuon_matrix_t* W, const himuon_matrix_t* M,
+                                 const himuon_matrix_t* G, int32_t n, int32_t T, int32_t K,
+                                 const float* abc, float mu, float eta, himuon_dtype_t dt,
+                                 float eps, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static description of a status code (never NULL). */
+const char* himuon_status_string(himuon_status_t s);
+
+/* hipError_t of the most recent HIMUON_ERR_HIP on this thread (0 if none). */
+int32_t himuon_last_hip_error(void);
+
+/* Library version as major * 10000 + minor * 100 + patch. */
+int32_t himuon_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HIMUON_H */

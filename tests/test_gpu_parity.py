@@ -1,0 +1,311 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Per-tile relative Frobenius error, max over the tiles checked:
+<= 3e-2 for bf16 data and <= 1e-4 for fp32 data.  Small cases are compared
+tile by tile over the whole matrix; the full-size workloads are compared on
+sampled tiles (edge tiles always included), with the input tiles copied to
+the host before the in-place call.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import tiled_newton_schulz_amd as H
+import workloads
+from workloads import COEFFS, WORKLOADS
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": 3e-2, "fp32": 1e-4}
+MIXED = [(3.4445, -4.7750, 2.0315), (2.8, -3.1, 1.2), (1.9, -1.3, 0.4), (1.6, -0.9, 0.3), (3.0, -3.2, 1.2)]
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def to_np(t):
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def run(mats, T, K=5, abc=COEFFS, cap=None):
+    H.himuon_tiled_ns(mats, T, K, abc, workspace_bytes=cap)
+    torch.cuda.synchronize()
+
+
+def full_check(x_host, T, dt, K=5, abc=COEFFS, cap=None, device="cuda"):
+    """Run one matrix on the GPU and compare every tile with the oracle."""
+    ref = oracle.tiled_ns(x_host.double().numpy(), T, abc, K=K)
+    g = x_host.to(device)
+    run([g], T, K, abc, cap)
+    err = oracle.tile_rel_errors(to_np(g), ref, T)
+    return err.max(), g
+
+
+def sample_tiles(H_, W_, T, n, rng):
+    th, tw = math.ceil(H_ / T), math.ceil(W_ / T)
+    pick = {(th - 1, tw - 1), (0, 0), (th - 1, 0), (0, tw - 1)}
+    while len(pick) < min(n, th * tw):
+        pick.add((int(rng.integers(th)), int(rng.integers(tw))))
+    return sorted(pick)
+
+
+def check_sampled(inputs_host_tiles, outputs, T, coeffs, K, tol):
+    """inputs_host_tiles: list of (matrix index, ti, tj, tile float64)."""
+    worst = 0.0
+    for mi, ti, tj, tile in inputs_host_tiles:
+        ref = oracle.ns_map(tile, coeffs, K=K)
+        h, w = tile.shape
+        got = to_np(outputs[mi][ti * T:ti * T + h, tj * T:tj * T + w])
+        worst = max(worst, oracle.tile_rel_error(got, ref))
+    assert worst <= tol, worst
+    return worst
+
+
+def grab(mats, T, per_matrix, rng, which=None):
+    out = []
+    for mi, m in enumerate(mats):
+        if which is not None and mi not in which:
+            continue
+        Hh, Ww = m.shape
+        for ti, tj in sample_tiles(Hh, Ww, T, per_matrix, rng):
+            tile = to_np(m[ti * T:min(ti * T + T, Hh), tj * T:min(tj * T + T, Ww)])
+            out.append((mi, ti, tj, tile))
+    return out
+
+
+# ---------------------------------------------------------------- small cases
+@pytest.mark.parametrize("T", [64, 128])
+def test_fp32_256x512_seed0(cuda, T):
+    w = WORKLOADS["fp32_256x512"]
+    x = workloads.host_tensors(w)[0]
+    say(f"fp32 256x512 T={T}")
+    err, _ = full_check(x, T, "fp32")
+    say(f"  max err {err:.3e}")
+    assert err <= TOL["fp32"]
+
+
+SHAPES = [(1, 1), (7, 300), (300, 7), (33, 65), (128, 128), (200, 150), (129, 257), (300, 299)]
+
+
+@pytest.mark.parametrize("T", [16, 32, 40, 64, 100, 128])
+def test_bf16_on_chip_shapes(cuda, T):
+    rng = np.random.default_rng([11, T])
+    for (h, w) in SHAPES:
+        x = workloads.round_to(rng.standard_normal((h, w)), "bf16")
+        err, _ = full_check(x, T, "bf16")
+        say(f"bf16 {h}x{w} T={T}: {err:.3e}")
+        assert err <= TOL["bf16"], (h, w, T, err)
+
+
+@pytest.mark.parametrize("T", [160, 256, 512, 4096])
+def test_bf16_step_path_shapes(cuda, T):
+    rng = np.random.default_rng([12, T])
+    for (h, w) in [(300, 299), (129, 600), (600, 130), (513, 257), (700, 520)]:
+        x = workloads.round_to(rng.standard_normal((h, w)), "bf16")
+        err, _ = full_check(x, T, "bf16")
+        say(f"bf16 {h}x{w} T={T}: {err:.3e}")
+        assert err <= TOL["bf16"], (h, w, T, err)
+
+
+@pytest.mark.parametrize("T", [8, 32, 64, 128, 256, 1000])
+def test_fp32_shapes(cuda, T):
+    rng = np.random.default_rng([13, T])
+    for (h, w) in [(1, 1), (33, 65), (200, 150), (300, 299), (129, 600)]:
+        x = workloads.round_to(rng.standard_normal((h, w)), "fp32")
+        err, _ = full_check(x, T, "fp32")
+        say(f"fp32 {h}x{w} T={T}: {err:.3e}")
+        assert err <= TOL["fp32"], (h, w, T, err)
+
+
+@pytest.mark.parametrize("dt,T", [("bf16", 32), ("bf16", 64), ("bf16", 128), ("bf16", 256), ("fp32", 64)])
+@pytest.mark.parametrize("K", [0, 1, 2, 5])
+def test_step_counts_and_mixed_coefficients(cuda, dt, T, K):
+    rng = np.random.default_rng([14, K, T])
+    x = workloads.round_to(rng.standard_normal((2 * T + 17, T + 9)), dt)
+    err, _ = full_check(x, T, dt, K=K, abc=MIXED[:K] if K else [])
+    say(f"{dt} K={K} T={T}: {err:.3e}")
+    assert err <= TOL[dt]
+
+
+def test_zero_and_tiny_tiles(cuda):
+    for dt in ("bf16", "fp32"):
+        for T in (64, 256):
+            x = torch.zeros(300, 200, dtype=torch.bfloat16 if dt == "bf16" else torch.float32)
+            x[:T, :T] = workloads.round_to(np.random.default_rng(3).standard_normal((T, T)) * 1e-3, dt)
+            err, g = full_check(x, T, dt)
+            assert err <= TOL[dt]
+            assert torch.count_nonzero(g[T:, :]) == 0 and torch.count_nonzero(g[:, T:]) == 0
+
+
+# ------------------------------------------------------------- invariants
+@pytest.mark.parametrize("dt,T", [("bf16", 32), ("bf16", 128), ("bf16", 256), ("fp32", 64)])
+def test_deterministic_and_tile_independent(cuda, dt, T):
+    rng = np.random.default_rng([15, T])
+    x = workloads.round_to(rng.standard_normal((3 * T + 5, 2 * T + 3)), dt).cuda()
+    a, b = x.clone(), x.clone()
+    run([a], T)
+    run([b], T)
+    assert torch.equal(a, b), "two runs differ"
+    c = x.clone()
+    c[T:2 * T, T:2 * T] *= -1.5
+    c[T + 3, T + 4] = float("nan")
+    run([c], T)
+    mask = torch.zeros_like(c, dtype=torch.bool)
+    mask[T:2 * T, T:2 * T] = True
+    assert torch.equal(a[~mask], c[~mask]), "a change in one tile leaked into others"
+    assert torch.isnan(c[mask]).all()
+
+
+@pytest.mark.parametrize("dt,T", [("bf16", 64), ("bf16", 256), ("fp32", 128)])
+def test_transposed_view_and_batch(cuda, dt, T):
+    rng = np.random.default_rng([16, T])
+    xs = [workloads.round_to(rng.standard_normal(s), dt).cuda() for s in [(300, 170), (170, 300), (64, 64)]]
+    ref = [x.clone() for x in xs]
+    for r in ref:
+        run([r], T)
+    batch = [x.clone() for x in xs]
+    run(batch, T)
+    for r, b_ in zip(ref, batch):
+        assert torch.equal(r, b_), "batched call differs from single calls"
+    # a transposed view is processed as the transpose of its storage
+    base = xs[0].clone()
+    view = base.t()
+    run([view], T)
+    expect = xs[0].clone()
+    run([expect], T)
+    assert torch.equal(base, expect)
+
+
+def test_column_blocks_of_fused_tensor(cuda):
+    """Sub-matrix descriptors (functional blocks of a fused Q|K|V tensor) are
+    processed as separate matrices, in one call."""
+    rng = np.random.default_rng(17)
+    fused = workloads.round_to(rng.standard_normal((256, 3 * 192)), "bf16").cuda()
+    parts = [fused[:, i * 192:(i + 1) * 192] for i in range(3)]
+    sep = [p.clone() for p in parts]
+    run(sep, 64)
+    run(parts, 64)
+    for p, s_ in zip(parts, sep):
+        assert torch.equal(p, s_)
+
+
+@pytest.mark.parametrize("cap_tiles", [1, 3, 7])
+def test_chunking_bit_exact(cuda, cap_tiles):
+    rng = np.random.default_rng([18, cap_tiles])
+    xs = [workloads.round_to(rng.standard_normal(s), "bf16").cuda() for s in [(600, 520), (257, 513)]]
+    full, mn = H.himuon_workspace_size(xs, 256, H.BF16)
+    a = [x.clone() for x in xs]
+    run(a, 256)
+    b = [x.clone() for x in xs]
+    run(b, 256, cap=mn * cap_tiles)
+    for u, v in zip(a, b):
+        assert torch.equal(u, v)
+
+
+# ------------------------------------------------------------- Muon step
+@pytest.mark.parametrize("dt,T", [("bf16", 64), ("bf16", 128), ("bf16", 256), ("fp32", 64), ("fp32", 256)])
+@pytest.mark.parametrize("K", [0, 5])
+def test_muon_step(cuda, dt, T, K):
+    rng = np.random.default_rng([19, T, K])
+    shape = (300, 170)
+    W = workloads.round_to(rng.standard_normal(shape), dt)
+    M = workloads.round_to(rng.standard_normal(shape), dt)
+    G = workloads.round_to(rng.standard_normal(shape), dt)
+    mu, eta = 0.95, 0.02
+    Wg, Mg, Gg = W.cuda(), M.cuda(), G.cuda()
+    H.himuon_muon_step([Wg], [Mg], [Gg], T, K, COEFFS, mu=mu, eta=eta)
+    torch.cuda.synchronize()
+    # momentum: mu M + G rounded once to the dtype (one ulp allows for the
+    # fp32-versus-fp64 evaluation before the rounding)
+    m_new = workloads.round_to(mu * M.double().numpy() + G.double().numpy(), dt).double()
+    ulp = m_new.abs() * (2.0 ** -7 if dt == "bf16" else 2.0 ** -23)
+    assert bool(((Mg.cpu().double() - m_new).abs() <= ulp).all()), "momentum differs by more than one ulp"
+    # weights: W - eta * tiledNS(M) with M as stored; per tile the difference
+    # is bounded by W's own rounding plus eta times the map's tolerance
+    U = oracle.tiled_ns(Mg.cpu().double().numpy(), T, COEFFS, K=K)
+    want = W.double().numpy() - eta * U
+    got = Wg.cpu().double().numpy()
+    half_ulp = np.abs(want) * (2.0 ** -8 if dt == "bf16" else 2.0 ** -24)
+    worst = 0.0
+    for r0, r1, c0, c1 in oracle.tile_grid(*shape, T):
+        d = np.linalg.norm(got[r0:r1, c0:c1] - want[r0:r1, c0:c1])
+        bound = np.linalg.norm(half_ulp[r0:r1, c0:c1]) + eta * TOL[dt] * np.linalg.norm(U[r0:r1, c0:c1])
+        worst = max(worst, d / bound)
+    say(f"muon {dt} T={T} K={K}: worst difference / bound = {worst:.3f}")
+    assert worst <= 1.0
+
+
+# ------------------------------------------------------------- workloads
+def test_layer_d2048(cuda):
+    """One transformer layer (Q, K, V, O, MLP x3) at T = 128, one launch."""
+    w = WORKLOADS["layer_d2048"]
+    mats = [t.cuda() for t in workloads.host_tensors(w)]
+    rng = np.random.default_rng(21)
+    sampled = grab(mats, 128, 40, rng)
+    say(f"layer_d2048: {len(sampled)} sampled tiles")
+    run(mats, 128)
+    worst = check_sampled(sampled, mats, 128, COEFFS, 5, TOL["bf16"])
+    say(f"  max err {worst:.3e}")
+
+
+@pytest.mark.parametrize("T", [32, 64, 128, 256])
+def test_layers24_d2048(cuda, T):
+    w = WORKLOADS["layers24_d2048"]
+    mats = workloads.device_tensors(w)
+    rng = np.random.default_rng([22, T])
+    which = set(int(i) for i in rng.choice(len(mats), 12, replace=False)) | {0, 6, 167}
+    sampled = grab(mats, T, 12, rng, which)
+    say(f"layers24 T={T}: {len(sampled)} sampled tiles")
+    run(mats, T)
+    worst = check_sampled(sampled, mats, T, COEFFS, 5, TOL["bf16"])
+    say(f"  max err {worst:.3e}")
+
+
+def test_layers24_full_matrix(cuda):
+    """The full-matrix map (T = max dims) on the 24-layer batch; three
+    matrices (one of each shape) are checked against the oracle."""
+    w = WORKLOADS["layers24_d2048"]
+    mats = workloads.device_tensors(w)
+    idx = [3, 4, 6]
+    host = {i: to_np(mats[i]) for i in idx}
+    say("layers24 full-matrix")
+    run(mats, 5632)
+    for i in idx:
+        ref = oracle.full_matrix_ns(host[i], COEFFS, K=5)
+        e = oracle.tile_rel_error(to_np(mats[i]), ref)
+        say(f"  matrix {i} {host[i].shape}: {e:.3e}")
+        assert e <= TOL["bf16"]
+
+
+def test_moe64_ragged(cuda):
+    w = WORKLOADS["moe64"]
+    mats = workloads.device_tensors(w)
+    rng = np.random.default_rng(23)
+    sampled = grab(mats, 256, 10, rng, {0, 1, 62, 127})
+    assert any(t.shape != (256, 256) for _, _, _, t in sampled)
+    say(f"moe64: {len(sampled)} sampled tiles")
+    run(mats, 256)
+    worst = check_sampled(sampled, mats, 256, COEFFS, 5, TOL["bf16"])
+    say(f"  max err {worst:.3e}")
+
+
+@pytest.mark.parametrize("T", [128, 256, 512])
+def test_dense8192_cap(cuda, T):
+    w = WORKLOADS["dense8192"]
+    mats = workloads.device_tensors(w)
+    rng = np.random.default_rng([24, T])
+    sampled = grab(mats, T, 6, rng)
+    say(f"dense8192 T={T}: {len(sampled)} sampled tiles, cap 4 GiB")
+    ref_mats = [m.clone() for m in mats] if T == 512 else None
+    run(mats, T, cap=4 << 30)
+    worst = check_sampled(sampled, mats, T, COEFFS, 5, TOL["bf16"])
+    say(f"  max err {worst:.3e}")
+    if ref_mats is not None:
+        # chunked (4 GiB) and a single chunk give the same bits
+        run(ref_mats, T, cap=1 << 40)
+        for a, b in zip(mats, ref_mats):
+            assert torch.equal(a, b)

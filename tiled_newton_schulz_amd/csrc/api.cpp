@@ -1,0 +1,517 @@
+// C ABI of the tiled Newton-Schulz library: argument validation, the tile
+// planner (launch groups, on-chip kernel choice, workspace chunks) and
+// dispatch.  See include/himuon.h for the contract.
+#include "himuon.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <vector>
+
+#include "common.h"
+
+using namespace himuon;
+
+namespace {
+
+thread_local int32_t g_last_hip = 0;
+
+constexpr int kWgNormMax = 32;
+constexpr size_t kAlign = 256;
+
+size_t elem_size(himuon_dtype_t dt) { return dt == HIMUON_BF16 ? 2 : 4; }
+size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+struct MatSpec {
+    void* m;
+    void* w;
+    const void* g;
+    int64_t rows, cols, m_ld, w_ld, g_ld;
+    int64_t tiles;   // tiles of this matrix
+};
+
+// ---- validation --------------------------------------------------------
+himuon_status_t check_matrix(const himuon_matrix_t& d, size_t es) {
+    if (d.ptr == nullptr) return HIMUON_ERR_INVALID_ARGUMENT;
+    if (d.rows < 1 || d.cols < 1 || d.ld < d.cols) return HIMUON_ERR_INVALID_ARGUMENT;
+    if (d.rows > INT32_MAX || d.cols > INT32_MAX) return HIMUON_ERR_LAYOUT;
+    if ((reinterpret_cast<uintptr_t>(d.ptr) % es) != 0) return HIMUON_ERR_LAYOUT;
+    // extent in bytes must fit in int64
+    const double ext = ((double)(d.rows - 1) * (double)d.ld + (double)d.cols) * (double)es;
+    if (ext > 9.0e18) return HIMUON_ERR_LAYOUT;
+    return HIMUON_OK;
+}
+
+struct Extent {
+    uintptr_t lo, hi;  // [lo, hi) bytes
+    int64_t ld, cols;
+    int64_t rows;
+    size_t es;
+    int id;
+};
+
+// True if two matrices share an element.  Byte ranges that overlap can still
+// be disjoint when both use the same row stride and occupy different column
+// ranges of the same rows (column blocks of one fused tensor).
+bool share_element(const Extent& a, const Extent& b) {
+    if (a.hi <= b.lo || b.hi <= a.lo) return false;
+    if (a.ld != b.ld || a.es != b.es) return true;
+    const Extent& x = a.lo <= b.lo ? a : b;
+    const Extent& y = a.lo <= b.lo ? b : a;
+    const uintptr_t d = y.lo - x.lo;
+    const uintptr_t row_bytes = (uintptr_t)x.ld * x.es;
+    if (d % x.es != 0) return true;
+    const int64_t dc = (int64_t)((d % row_bytes) / x.es);   // column offset of y inside x's rows
+    // y's columns [dc, dc + y.cols) must avoid x's [0, x.cols) in every row both touch,
+    // including y rows that wrap past ld.
+    if (dc < x.cols) return true;
+    if (dc + y.cols > x.ld) return true;   // wraps into x's next row
+    return false;
+}
+
+himuon_status_t check_overlap(std::vector<Extent>& ex) {
+    std::sort(ex.begin(), ex.end(), [](const Extent& a, const Extent& b) { return a.lo < b.lo; });
+    for (size_t i = 0; i < ex.size(); ++i)
+        for (size_t j = i + 1; j < ex.size() && ex[j].lo < ex[i].hi; ++j)
+            if (share_element(ex[i], ex[j])) return HIMUON_ERR_OVERLAP;
+    return HIMUON_OK;
+}
+
+Extent extent_of(const himuon_matrix_t& d, size_t es, int id) {
+    Extent e;
+    e.lo = reinterpret_cast<uintptr_t>(d.ptr);
+    e.hi = e.lo + (uintptr_t)(((d.rows - 1) * d.ld + d.cols) * (int64_t)es);
+    e.ld = d.ld;
+    e.cols = d.cols;
+    e.rows = d.rows;
+    e.es = es;
+    e.id = id;
+    return e;
+}
+
+himuon_status_t check_common(int32_t n, int32_t T, int32_t K, himuon_dtype_t dt, float eps) {
+    if (n < 0 || T < 1) return HIMUON_ERR_INVALID_ARGUMENT;
+    if (K < 0 || K > HIMUON_MAX_STEPS) return HIMUON_ERR_INVALID_ARGUMENT;
+    if (dt != HIMUON_BF16 && dt != HIMUON_FP32) return HIMUON_ERR_UNSUPPORTED;
+    if (!(eps >= 0.f) || !std::isfinite(eps)) return HIMUON_ERR_INVALID_ARGUMENT;
+    return HIMUON_OK;
+}
+
+himuon_status_t check_abc(int32_t K, const float* abc) {
+    if (K > 0) {
+        if (abc == nullptr) return HIMUON_ERR_INVALID_ARGUMENT;
+        for (int i = 0; i < 3 * K; ++i)
+            if (!std::isfinite(abc[i])) return HIMUON_ERR_INVALID_ARGUMENT;
+    }
+    return HIMUON_OK;
+}
+
+// ---- planning ------------------------------------------------------------
+// Each matrix is cut into up to four tile classes (interior T x T tiles, the
+// right-edge column, the bottom-edge row and the corner); all tiles of a class
+// share one shape, and each class is routed by that shape:
+//   bf16, both sides 32..128          -> on-chip kernel (kernel tile 32/64/128)
+//   bf16, a side < 32, both <= 64     -> on-chip kernel, hi/lo split precision
+//   bf16, both sides >= 32, one > 128 -> step path, bf16 workspace
+//   bf16, a side < 32, one > 64       -> step path, fp32 workspace
+//   fp32                              -> step path, fp32 workspace
+struct TileClass {
+    int spec;                 // matrix index
+    int32_t ti0, tj0, n_ti, n_tj, th, tw;
+    int64_t tiles() const { return (int64_t)n_ti * n_tj; }
+};
+
+enum class Route { OnChip, OnChipPrecise, StepBf16, StepFp32 };
+
+Route route_of(himuon_dtype_t dt, int32_t th, int32_t tw) {
+    const int32_t mn = std::min(th, tw), mx = std::max(th, tw);
+    if (dt == HIMUON_FP32) return Route::StepFp32;
+    if (mx <= 128 && mn >= 32) return Route::OnChip;
+    if (mx <= 64) return Route::OnChipPrecise;
+    if (mn >= 32) return Route::StepBf16;
+    return Route::StepFp32;
+}
+int kernel_tile_for(int32_t th, int32_t tw) {
+    const int32_t e = std::max(th, tw);
+    return e <= 32 ? 32 : e <= 64 ? 64 : 128;
+}
+int64_t tiles_of(int64_t rows, int64_t cols, int32_t T) {
+    return ((rows + T - 1) / T) * ((cols + T - 1) / T);
+}
+
+void classes_of(const MatSpec& s, int idx, int32_t T, std::vector<TileClass>& out) {
+    const int32_t fh = (int32_t)(s.rows / T), fw = (int32_t)(s.cols / T);
+    const int32_t rh = (int32_t)(s.rows % T), rw = (int32_t)(s.cols % T);
+    if (fh > 0 && fw > 0) out.push_back({idx, 0, 0, fh, fw, T, T});
+    if (fh > 0 && rw > 0) out.push_back({idx, 0, fw, fh, 1, T, rw});
+    if (rh > 0 && fw > 0) out.push_back({idx, fh, 0, 1, fw, rh, T});
+    if (rh > 0 && rw > 0) out.push_back({idx, fh, fw, 1, 1, rh, rw});
+}
+
+struct Chunk {
+    int group;          // index into step groups
+    int32_t tb, te;     // tile range within the group
+    int64_t xbase, abase, xel, ael;
+    int32_t rmax, smax, sbmax;
+};
+
+struct Group {
+    std::vector<TileClass> cls;
+    std::vector<int64_t> tile_base, xoff, aoff;
+    int kernel_tile = 0;         // on-chip groups
+    bool precise = false;        // on-chip groups
+    int wk = 0;                  // step groups: workspace dtype (0 bf16, 1 fp32)
+    int64_t tiles = 0;
+};
+
+struct Plan {
+    std::vector<Group> rgroups;  // on-chip launches
+    std::vector<Group> sgroups;  // step-by-step groups
+    std::vector<Chunk> chunks;
+    size_t ws_full = 0, ws_min = 0;
+    int64_t tiles = 0;
+    int64_t launches = 0;
+};
+
+size_t chunk_bytes(int64_t xel, int64_t ael, int64_t tiles, size_t es) {
+    return align_up((size_t)xel * es) * 2 + align_up((size_t)ael * es) * 2 + align_up((size_t)tiles * kWgNormMax * 4);
+}
+
+void oriented(const TileClass& c, int32_t& r, int32_t& sd) {
+    r = std::min(c.th, c.tw);
+    sd = std::max(c.th, c.tw);
+}
+
+// Builds the plan.  With enforce_cap, every chunk's workspace stays within
+// `cap` (HIMUON_ERR_WORKSPACE if one tile alone does not fit).
+himuon_status_t build_plan(const std::vector<MatSpec>& specs, int32_t T, int32_t K, himuon_dtype_t dt,
+                           size_t cap, bool enforce_cap, Plan& plan) {
+    plan = Plan();
+    std::vector<TileClass> all;
+    for (size_t i = 0; i < specs.size(); ++i) {
+        plan.tiles += specs[i].tiles;
+        classes_of(specs[i], (int)i, T, all);
+    }
+
+    // on-chip launches, keyed by (kernel tile, precision)
+    for (int precise = 0; precise < 2; ++precise)
+        for (int kt : {32, 64, 128}) {
+            Group cur;
+            cur.kernel_tile = kt;
+            cur.precise = precise != 0;
+            for (const TileClass& c : all) {
+                const Route r = route_of(dt, c.th, c.tw);
+                const bool on = precise ? r == Route::OnChipPrecise : r == Route::OnChip;
+                if (!on || kernel_tile_for(c.th, c.tw) != kt) continue;
+                if ((int)cur.cls.size() == kGroup || cur.tiles + c.tiles() > INT32_MAX) {
+                    plan.rgroups.push_back(cur);
+                    cur = Group();
+                    cur.kernel_tile = kt;
+                    cur.precise = precise != 0;
+                }
+                cur.cls.push_back(c);
+                cur.tile_base.push_back(cur.tiles);
+                cur.tiles += c.tiles();
+            }
+            if (!cur.cls.empty()) plan.rgroups.push_back(cur);
+        }
+    plan.launches = (int64_t)plan.rgroups.size();
+
+    // step groups, keyed by workspace dtype
+    for (int wk = 0; wk < 2; ++wk) {
+        Group cur;
+        cur.wk = wk;
+        int64_t xo = 0, ao = 0;
+        for (const TileClass& c : all) {
+            const Route r = route_of(dt, c.th, c.tw);
+            if (!((wk == 0 && r == Route::StepBf16) || (wk == 1 && r == Route::StepFp32))) continue;
+            if ((int)cur.cls.size() == kGroup || cur.tiles + c.tiles() > INT32_MAX / 64) {
+                plan.sgroups.push_back(cur);
+                cur = Group();
+                cur.wk = wk;
+                xo = ao = 0;
+            }
+            int32_t rr, ss;
+            oriented(c, rr, ss);
+            cur.cls.push_back(c);
+            cur.tile_base.push_back(cur.tiles);
+            cur.xoff.push_back(xo);
+            cur.aoff.push_back(ao);
+            cur.tiles += c.tiles();
+            xo += c.tiles() * rr * round8(ss);
+            ao += c.tiles() * rr * round8(rr);
+        }
+        if (!cur.cls.empty()) plan.sgroups.push_back(cur);
+    }
+    for (size_t gi = 0; gi < plan.sgroups.size(); ++gi) {
+        const Group& G = plan.sgroups[gi];
+        const size_t es = G.wk == 0 ? 2 : 4;
+        Chunk ch{};
+        bool open = false;
+        for (size_t k = 0; k < G.cls.size(); ++k) {
+            const TileClass& c = G.cls[k];
+            int32_t rr, ss;
+            oriented(c, rr, ss);
+            const int64_t xe = (int64_t)rr * round8(ss), ae = (int64_t)rr * round8(rr);
+            const int32_t sb = ((c.th + 63) / 64) * ((c.tw + 63) / 64);
+            const size_t one = chunk_bytes(xe, ae, 1, es);
+            plan.ws_min = std::max(plan.ws_min, one);
+            for (int64_t lt = 0; lt < c.tiles(); ++lt) {
+                const int32_t t = (int32_t)(G.tile_base[k] + lt);
+                if (open && enforce_cap && chunk_bytes(ch.xel + xe, ch.ael + ae, t + 1 - ch.tb, es) > cap) {
+                    plan.chunks.push_back(ch);
+                    open = false;
+                }
+                if (!open) {
+                    if (enforce_cap && one > cap) return HIMUON_ERR_WORKSPACE;
+                    ch = Chunk{};
+                    ch.group = (int)gi;
+                    ch.tb = t;
+                    ch.xbase = G.xoff[k] + lt * xe;
+                    ch.abase = G.aoff[k] + lt * ae;
+                    open = true;
+                }
+                ch.te = t + 1;
+                ch.xel += xe;
+                ch.ael += ae;
+                ch.rmax = std::max(ch.rmax, rr);
+                ch.smax = std::max(ch.smax, ss);
+                ch.sbmax = std::max(ch.sbmax, sb);
+            }
+        }
+        if (open) plan.chunks.push_back(ch);
+    }
+    for (const auto& c : plan.chunks) {
+        const size_t es = plan.sgroups[c.group].wk == 0 ? 2 : 4;
+        plan.ws_full = std::max(plan.ws_full, chunk_bytes(c.xel, c.ael, c.te - c.tb, es));
+        plan.launches += 2 + 3LL * K;
+    }
+    return HIMUON_OK;
+}
+
+himuon_status_t gather(const himuon_matrix_t* W, const himuon_matrix_t* M, const himuon_matrix_t* G,
+                       int32_t n, int32_t T, himuon_dtype_t dt, std::vector<MatSpec>& specs) {
+    const size_t es = elem_size(dt);
+    specs.clear();
+    if (n > 0 && M == nullptr) return HIMUON_ERR_INVALID_ARGUMENT;
+    const bool muon = W != nullptr || G != nullptr;
+    if (muon && (W == nullptr || G == nullptr)) return HIMUON_ERR_INVALID_ARGUMENT;
+    std::vector<Extent> written, read;
+    for (int i = 0; i < n; ++i) {
+        himuon_status_t st = check_matrix(M[i], es);
+        if (st != HIMUON_OK) return st;
+        MatSpec s{};
+        s.m = M[i].ptr;
+        s.rows = M[i].rows;
+        s.cols = M[i].cols;
+        s.m_ld = M[i].ld;
+        written.push_back(extent_of(M[i], es, i));
+        if (muon) {
+            if ((st = check_matrix(W[i], es)) != HIMUON_OK) return st;
+            if ((st = check_matrix(G[i], es)) != HIMUON_OK) return st;
+            if (W[i].rows != M[i].rows || W[i].cols != M[i].cols || G[i].rows != M[i].rows ||
+                G[i].cols != M[i].cols)
+                return HIMUON_ERR_INVALID_ARGUMENT;
+            s.w = W[i].ptr;
+            s.w_ld = W[i].ld;
+            s.g = G[i].ptr;
+            s.g_ld = G[i].ld;
+            written.push_back(extent_of(W[i], es, n + i));
+            read.push_back(extent_of(G[i], es, 2 * n + i));
+        }
+        s.tiles = tiles_of(s.rows, s.cols, T);
+        if (s.tiles > INT32_MAX / 64) return HIMUON_ERR_LAYOUT;
+        specs.push_back(s);
+    }
+    std::vector<Extent> all = written;
+    if (check_overlap(all) != HIMUON_OK) return HIMUON_ERR_OVERLAP;
+    // a read-only gradient may alias nothing that is written
+    for (const auto& r : read)
+        for (const auto& w : written)
+            if (share_element(r, w)) return HIMUON_ERR_OVERLAP;
+    return HIMUON_OK;
+}
+
+MatEntry entry_of(const MatSpec& s, const TileClass& c, int64_t tile_base, int64_t xoff, int64_t aoff) {
+    MatEntry e{};
+    e.m = s.m;
+    e.w = s.w;
+    e.g = s.g;
+    e.m_ld = s.m_ld;
+    e.w_ld = s.w_ld;
+    e.g_ld = s.g_ld;
+    e.xoff = xoff;
+    e.aoff = aoff;
+    e.ti0 = c.ti0;
+    e.tj0 = c.tj0;
+    e.n_tj = c.n_tj;
+    e.th = c.th;
+    e.tw = c.tw;
+    e.tile_base = (int32_t)tile_base;
+    return e;
+}
+
+himuon_status_t hip_fail(hipError_t e) {
+    g_last_hip = (int32_t)e;
+    return HIMUON_ERR_HIP;
+}
+
+himuon_status_t run(const std::vector<MatSpec>& specs, int32_t T, int32_t K, const float* abc,
+                    himuon_dtype_t dt, float eps, float mu, float eta, bool muon, void* ws, size_t ws_bytes,
+                    void* stream) {
+    if (specs.empty()) return HIMUON_OK;
+    if (ws_bytes > 0 && ws == nullptr) return HIMUON_ERR_WORKSPACE;
+    Plan plan;
+    himuon_status_t st = build_plan(specs, T, K, dt, ws_bytes, true, plan);
+    if (st != HIMUON_OK) return st;
+    if (!plan.chunks.empty() && ws == nullptr) return HIMUON_ERR_WORKSPACE;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+
+    for (const Group& G : plan.rgroups) {
+        ResidentArgs a{};
+        a.nmats = (int32_t)G.cls.size();
+        for (size_t k = 0; k < G.cls.size(); ++k)
+            a.mats[k] = entry_of(specs[G.cls[k].spec], G.cls[k], G.tile_base[k], 0, 0);
+        for (int i = 0; i < 3 * K; ++i) a.abc[i] = abc[i];
+        a.total_tiles = (int32_t)G.tiles;
+        a.T = T;
+        a.K = K;
+        a.eps = eps;
+        a.mu = mu;
+        a.eta = eta;
+        hipError_t e = launch_resident(a, G.kernel_tile, muon, G.precise, s);
+        if (e != hipSuccess) return hip_fail(e);
+    }
+
+    for (const Chunk& c : plan.chunks) {
+        const Group& G = plan.sgroups[c.group];
+        const size_t es = G.wk == 0 ? 2 : 4;
+        StepArgs a{};
+        a.nmats = (int32_t)G.cls.size();
+        for (size_t k = 0; k < G.cls.size(); ++k)
+            a.mats[k] = entry_of(specs[G.cls[k].spec], G.cls[k], G.tile_base[k], G.xoff[k], G.aoff[k]);
+        for (int i = 0; i < 3 * K; ++i) a.abc[i] = abc[i];
+        a.T = T;
+        a.K = K;
+        a.tile_begin = c.tb;
+        a.tile_end = c.te;
+        a.xbase = c.xbase;
+        a.abase = c.abase;
+        a.nb_max = (c.rmax + 127) / 128;
+        a.ns_max = (c.smax + 127) / 128;
+        a.wg_norm = std::min(kWgNormMax, std::max(1, c.sbmax));
+        a.io_dtype = dt == HIMUON_BF16 ? 0 : 1;
+        a.wk_dtype = G.wk;
+        a.muon = muon ? 1 : 0;
+        a.eps = eps;
+        a.mu = mu;
+        a.eta = eta;
+        char* base = reinterpret_cast<char*>(ws);
+        const size_t xb = align_up((size_t)c.xel * es), ab = align_up((size_t)c.ael * es);
+        a.Xc = base;
+        a.Xn = base + xb;
+        a.A = base + 2 * xb;
+        a.B = base + 2 * xb + ab;
+        a.partial = reinterpret_cast<float*>(base + 2 * xb + 2 * ab);
+        const int64_t nt = c.te - c.tb;
+        hipError_t e = launch_step_norm(a, s);
+        if (e != hipSuccess) return hip_fail(e);
+        for (int step = 0; step < K; ++step) {
+            a.step = step;
+            const int64_t tri = (int64_t)a.nb_max * (a.nb_max + 1) / 2;
+            a.grid_blocks = (int32_t)(((nt * tri) + 7) / 8 * 8);
+            if ((e = launch_step_gram(a, s)) != hipSuccess) return hip_fail(e);
+            if ((e = launch_step_poly(a, s)) != hipSuccess) return hip_fail(e);
+            a.grid_blocks = (int32_t)(((nt * a.nb_max * a.ns_max) + 7) / 8 * 8);
+            if ((e = launch_step_apply(a, s)) != hipSuccess) return hip_fail(e);
+            std::swap(a.Xc, a.Xn);
+        }
+    }
+    return HIMUON_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+himuon_status_t himuon_plan(const himuon_matrix_t* m, int32_t n, int32_t T, int32_t K, himuon_dtype_t dt,
+                            size_t workspace_bytes, himuon_plan_info_t* info) {
+    if (info == nullptr) return HIMUON_ERR_INVALID_ARGUMENT;
+    std::memset(info, 0, sizeof(*info));
+    himuon_status_t st = check_common(n, T, K, dt, 0.f);
+    if (st != HIMUON_OK) return st;
+    std::vector<MatSpec> specs;
+    if ((st = gather(nullptr, m, nullptr, n, T, dt, specs)) != HIMUON_OK) return st;
+    Plan plan;
+    if ((st = build_plan(specs, T, K, dt, workspace_bytes, true, plan)) != HIMUON_OK) return st;
+    info->tiles = plan.tiles;
+    info->resident_launches = (int64_t)plan.rgroups.size();
+    info->chunks = (int64_t)plan.chunks.size();
+    info->launches = plan.launches;
+    for (const auto& g : plan.rgroups) info->kernel_tile = std::max<int64_t>(info->kernel_tile, g.kernel_tile);
+    info->workspace_full = plan.ws_full;
+    info->workspace_min = plan.ws_min;
+    return HIMUON_OK;
+}
+
+himuon_status_t himuon_workspace_size(const himuon_matrix_t* m, int32_t n, int32_t T, himuon_dtype_t dt,
+                                      size_t* full, size_t* min) {
+    if (full) *full = 0;
+    if (min) *min = 0;
+    himuon_status_t st = check_common(n, T, 0, dt, 0.f);
+    if (st != HIMUON_OK) return st;
+    std::vector<MatSpec> specs;
+    if ((st = gather(nullptr, m, nullptr, n, T, dt, specs)) != HIMUON_OK) return st;
+    Plan plan;
+    if ((st = build_plan(specs, T, 0, dt, 0, false, plan)) != HIMUON_OK) return st;
+    if (full) *full = plan.ws_full;
+    if (min) *min = plan.ws_min;
+    return HIMUON_OK;
+}
+
+himuon_status_t himuon_tiled_ns(const himuon_matrix_t* m, int32_t n, int32_t T, int32_t K, const float* abc,
+                                himuon_dtype_t dt, float eps, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+    himuon_status_t st = check_common(n, T, K, dt, eps);
+    if (st != HIMUON_OK) return st;
+    if ((st = check_abc(K, abc)) != HIMUON_OK) return st;
+    std::vector<MatSpec> specs;
+    if ((st = gather(nullptr, m, nullptr, n, T, dt, specs)) != HIMUON_OK) return st;
+    return run(specs, T, K, abc, dt, eps, 0.f, 0.f, false, workspace, workspace_bytes, stream);
+}
+
+himuon_status_t himuon_muon_step(const himuon_matrix_t* W, const himuon_matrix_t* M, const himuon_matrix_t* G,
+                                 int32_t n, int32_t T, int32_t K, const float* abc, float mu, float eta,
+                                 himuon_dtype_t dt, float eps, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+    himuon_status_t st = check_common(n, T, K, dt, eps);
+    if (st != HIMUON_OK) return st;
+    if ((st = check_abc(K, abc)) != HIMUON_OK) return st;
+    if (!std::isfinite(mu) || !std::isfinite(eta)) return HIMUON_ERR_INVALID_ARGUMENT;
+    if (n > 0 && (W == nullptr || G == nullptr || M == nullptr)) return HIMUON_ERR_INVALID_ARGUMENT;
+    std::vector<MatSpec> specs;
+    if ((st = gather(n > 0 ? W : nullptr, M, n > 0 ? G : nullptr, n, T, dt, specs)) != HIMUON_OK) return st;
+    return run(specs, T, K, abc, dt, eps, mu, eta, true, workspace, workspace_bytes, stream);
+}
+
+const char* himuon_status_string(himuon_status_t s) {
+    switch (s) {
+        case HIMUON_OK: return "ok";
+        case HIMUON_ERR_INVALID_ARGUMENT: return "invalid argument";
+        case HIMUON_ERR_UNSUPPORTED: return "unsupported dtype or option";
+        case HIMUON_ERR_LAYOUT: return "bad layout (alignment or size)";
+        case HIMUON_ERR_OVERLAP: return "matrices overlap in memory";
+        case HIMUON_ERR_WORKSPACE: return "workspace too small or missing";
+        case HIMUON_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+int32_t himuon_last_hip_error(void) { return g_last_hip; }
+
+int32_t himuon_version(void) { return 10000; }
+
+}  // extern "C"

@@ -1,0 +1,482 @@
+// On-chip tiled Newton-Schulz for tiles up to 128 x 128 in bf16 on gfx950.
+//
+// One wavefront owns one tile for all K steps (HiMuon abstract: the same finite
+// Newton-Schulz map applied to every tile independently; Gram Newton-Schulz
+// page, Algorithm 1, for the map itself).  Tiles smaller than the kernel size
+// (edge tiles, or a grid T below 32/64/128) are zero padded: the padded Gram
+// matrix is block diagonal, so padded rows and columns stay exactly zero and
+// the real block evolves as its own map.
+//
+// Data layout of one 32 x 32 block in a wavefront (v_mfma_f32_32x32x16_bf16):
+//   accumulator layout (AL): lane l, register q holds M[rho(l,q)][l % 32],
+//     rho(l,q) = (q/4)*8 + (l/32)*4 + q%4;
+//   row layout (RL) = AL of the transpose: lane l holds M[l % 32][rho(l,q)].
+// Registers 8f..8f+7 of an AL block are a complete MFMA operand whose k index
+// h = (l/32)*8 + e stands for row 16f + 8(e/4) + 4(l/32) + e%4 of the block;
+// as long as both operands use that same k order the product is exact.
+//
+// Per step, with X (the tile) in RL:
+//   A(I,J)  = sum_K RL(X(I,K)) . RL(X(J,K))           -> AL(A)      (MFMA)
+//   A2(P,Q) = sum_K AL(A(K,P)) . AL(A(K,Q))  (A = A^T) -> AL(A^2)
+//   B       = b A + c A^2, from the same rounded A in both terms
+//   X'^T(J,I) = sum_K AL(X(K,J)) . AL(B(K,I)), started at a X -> RL(X')
+// AL(X) is read from LDS (X stored row-major, bf16) with ds_read_tr16_b64,
+// which gives the one transpose per step its 8-byte reads.
+//
+// Precision (bf16 MFMA operands, fp32 accumulation):
+//  * kernel tiles 32 and 64 keep the tile in fp32 registers; X' = a X starts
+//    from fp32 and X is rounded to bf16 only as an MFMA operand.  Kernel tile
+//    32 also carries B as a bf16 hi/lo pair (B X = B_hi X + B_lo X).
+//  * kernel tile 128 keeps the tile in LDS as bf16 and folds a X into the
+//    product, X' = (a I + B) X, equal in exact arithmetic, with a added to the
+//    diagonal of B before it is rounded.
+//  * PRECISE (tiles with a side below 32, where bf16 rounding of a small
+//    Gram matrix dominates): X, A and B all carried as bf16 hi/lo pairs, three
+//    products per contraction (the lo x lo term dropped).
+
+#include "common.h"
+
+namespace himuon {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
+
+#define LDS_AS __attribute__((address_space(3)))
+
+namespace {
+
+__device__ __forceinline__ float bf2f(unsigned short u) { return __uint_as_float(((unsigned)u) << 16); }
+__device__ __forceinline__ unsigned short f2bf(float f) {
+    __bf16 b = (__bf16)f;
+    return __builtin_bit_cast(unsigned short, b);
+}
+// Two floats -> one word of two bf16 (round to nearest even), low half first.
+__device__ __forceinline__ unsigned pack2(float a, float b) {
+    bf16x2 v = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(unsigned, v);
+}
+__device__ __forceinline__ float lo_f(unsigned u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float hi_f(unsigned u) { return __uint_as_float(u & 0xffff0000u); }
+
+// Registers off..off+7 of an accumulator block as one bf16 MFMA operand.
+__device__ __forceinline__ u32x4 cvt8(const f32x16& v, int off) {
+    u32x4 r;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) r[k] = pack2(v[off + 2 * k], v[off + 2 * k + 1]);
+    return r;
+}
+// The bf16 rounding error of those registers, itself rounded to bf16.
+__device__ __forceinline__ u32x4 cvt8_lo(const f32x16& v, int off, u32x4 hi) {
+    u32x4 r;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        r[k] = pack2(v[off + 2 * k] - lo_f(hi[k]), v[off + 2 * k + 1] - hi_f(hi[k]));
+    return r;
+}
+__device__ __forceinline__ f32x16 mfma32w(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                   c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+// Global <-> LDS tile movement in 16-byte chunks, masked to the h x w tile.
+template <int TK>
+struct TileIO {
+    static constexpr int CPR = TK / 8;            // chunks per row
+    static constexpr int NCH = TK * CPR / 64;     // chunks per lane
+
+    __device__ static u16x8 load(const unsigned short* base, int64_t ld, int r, int col, int h, int w, bool vec) {
+        u16x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (r < h) {
+            const unsigned short* p = base + (int64_t)r * ld + col;
+            if (vec && col + 8 <= w) {
+                v = *reinterpret_cast<const u16x8*>(p);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (col + e < w) v[e] = p[e];
+            }
+        }
+        return v;
+    }
+    __device__ static void store(unsigned short* base, int64_t ld, int r, int col, int h, int w, bool vec, u16x8 v) {
+        if (r < h) {
+            unsigned short* p = base + (int64_t)r * ld + col;
+            if (vec && col + 8 <= w) {
+                *reinterpret_cast<u16x8*>(p) = v;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (col + e < w) p[e] = v[e];
+            }
+        }
+    }
+};
+
+__device__ __forceinline__ bool vec_ok(const void* base, int64_t ld, int c0) {
+    return ((reinterpret_cast<uintptr_t>(base) & 15) == 0) && ((ld & 7) == 0) && ((c0 & 7) == 0);
+}
+
+}  // namespace
+
+template <int TK, bool MUON, bool PRECISE>
+__global__ __launch_bounds__(64) void resident_kernel(const ResidentArgs args) {
+    constexpr int NB = TK / 32;          // 32x32 blocks per side
+    constexpr int LD = TK + 8;           // LDS row stride (elements), 16-byte pad
+    constexpr bool MASTER32 = TK <= 64;  // fp32 copy of the tile in registers
+    constexpr bool SPLIT_X = PRECISE;
+    constexpr bool SPLIT_A = PRECISE;
+    constexpr bool SPLIT_B = PRECISE || TK == 32;
+    static_assert(!PRECISE || MASTER32, "hi/lo splitting needs the fp32 tile");
+    using IO = TileIO<TK>;
+
+    __shared__ __attribute__((aligned(16))) unsigned short sX[TK * LD];
+    __shared__ __attribute__((aligned(16))) unsigned short sXl[SPLIT_X ? TK * LD : 8];
+
+    const int lane = threadIdx.x;
+    const int l32 = lane & 31;
+    const int g = lane >> 5;
+
+    // ---- which tile: class by scalar scan of the launch table ----
+    const int t = blockIdx.x;
+    int mi = 0;
+    for (int i = 1; i < args.nmats; ++i)
+        if (t >= args.mats[i].tile_base) mi = i;
+    const MatEntry& me = args.mats[mi];
+    const TileGeom tg = class_tile(me, args.T, t - me.tile_base);
+    const int r0 = tg.r0, c0 = tg.c0, h = tg.h, w = tg.w;
+
+    unsigned short* mbase = reinterpret_cast<unsigned short*>(me.m) + (int64_t)r0 * me.m_ld + c0;
+    const bool mvec = vec_ok(me.m, me.m_ld, c0);
+
+    // ---- load (Muon: M <- mu M + G, stored), sum of squares ----
+    float ss = 0.f;
+    u16x8 chunk[IO::NCH];
+    {
+        const unsigned short* gbase = nullptr;
+        bool gvec = false;
+        if constexpr (MUON) {
+            gbase = reinterpret_cast<const unsigned short*>(me.g) + (int64_t)r0 * me.g_ld + c0;
+            gvec = vec_ok(me.g, me.g_ld, c0);
+        }
+#pragma unroll
+        for (int it = 0; it < IO::NCH; ++it) {
+            const int idx = it * 64 + lane;
+            const int r = idx / IO::CPR, col = (idx % IO::CPR) * 8;
+            u16x8 v = IO::load(mbase, me.m_ld, r, col, h, w, mvec);
+            if constexpr (MUON) {
+                u16x8 gv = IO::load(gbase, me.g_ld, r, col, h, w, gvec);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] = f2bf(args.mu * bf2f(v[e]) + bf2f(gv[e]));
+                IO::store(mbase, me.m_ld, r, col, h, w, mvec, v);
+            }
+            chunk[it] = v;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) { float x = bf2f(v[e]); ss += x * x; }
+        }
+    }
+    ss = wave_sum(ss);
+    const float scale = 1.0f / (sqrtf(ss) + args.eps);
+
+    // RL run (block I,J; run m = q/4): row I*32 + l32, cols J*32 + 8m + 4g .. +3
+    auto rl_off = [&](int I, int J, int m) { return (I * 32 + l32) * LD + J * 32 + 8 * m + 4 * g; };
+    auto put_rl = [&](unsigned short* buf, const u32x4 (&fr)[2], int I, int J) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            u32x2 v = {fr[m >> 1][2 * (m & 1)], fr[m >> 1][2 * (m & 1) + 1]};
+            *reinterpret_cast<u32x2*>(&buf[rl_off(I, J, m)]) = v;
+        }
+    };
+    // AL operand of block (K, J) of an LDS tile: two transposed 8-byte reads
+    auto tr_frag = [&](const unsigned short* buf, int K, int J, int f) {
+        const int G = lane >> 4, i16 = lane & 15;
+        const int col = J * 32 + 16 * (G & 1) + 4 * (i16 & 3);
+        const int rowb = K * 32 + 16 * f + 4 * g + (i16 >> 2);
+        bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(&buf[rowb * LD + col]));
+        bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(&buf[(rowb + 8) * LD + col]));
+        return __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+
+    f32x16 Xm[MASTER32 ? NB : 1][MASTER32 ? NB : 1];
+    if constexpr (MASTER32) {
+#pragma unroll
+        for (int it = 0; it < IO::NCH; ++it) {
+            const int idx = it * 64 + lane;
+            const int r = idx / IO::CPR, col = (idx % IO::CPR) * 8;
+            *reinterpret_cast<u16x8*>(&sX[r * LD + col]) = chunk[it];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int I = 0; I < NB; ++I)
+#pragma unroll
+            for (int J = 0; J < NB; ++J)
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    u16x4 v = *reinterpret_cast<const u16x4*>(&sX[rl_off(I, J, m)]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) Xm[I][J][4 * m + e] = bf2f(v[e]) * scale;
+                }
+        __syncthreads();
+    } else {
+#pragma unroll
+        for (int it = 0; it < IO::NCH; ++it) {
+            const int idx = it * 64 + lane;
+            const int r = idx / IO::CPR, col = (idx % IO::CPR) * 8;
+            u16x8 v;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = f2bf(bf2f(chunk[it][e]) * scale);
+            *reinterpret_cast<u16x8*>(&sX[r * LD + col]) = v;
+        }
+        __syncthreads();
+    }
+
+    // ---- K Newton-Schulz steps ----
+    for (int step = 0; step < args.K; ++step) {
+        const float ca = args.abc[3 * step], cb = args.abc[3 * step + 1], cc = args.abc[3 * step + 2];
+        u32x4 Abf[NB][NB][2];                       // AL(A), bf16 (hi)
+        u32x4 Alo[SPLIT_A ? NB : 1][SPLIT_A ? NB : 1][2];
+        u32x4 Bbf[NB][NB][2];                       // AL(B)
+        u32x4 Blo[SPLIT_B ? NB : 1][SPLIT_B ? NB : 1][2];
+
+        // A = X X^T (both operands are row fragments of X; A(J,I) is computed
+        // next to A(I,J) so that two accumulator chains run interleaved)
+        if constexpr (MASTER32) {
+            u32x4 XR[NB][NB][2];
+            u32x4 XL[SPLIT_X ? NB : 1][SPLIT_X ? NB : 1][2];
+#pragma unroll
+            for (int I = 0; I < NB; ++I)
+#pragma unroll
+                for (int J = 0; J < NB; ++J) {
+                    XR[I][J][0] = cvt8(Xm[I][J], 0);
+                    XR[I][J][1] = cvt8(Xm[I][J], 8);
+                    put_rl(sX, XR[I][J], I, J);
+                    if constexpr (SPLIT_X) {
+                        XL[I][J][0] = cvt8_lo(Xm[I][J], 0, XR[I][J][0]);
+                        XL[I][J][1] = cvt8_lo(Xm[I][J], 8, XR[I][J][1]);
+                        put_rl(sXl, XL[I][J], I, J);
+                    }
+                }
+#pragma unroll
+            for (int I = 0; I < NB; ++I)
+#pragma unroll
+                for (int J = I; J < NB; ++J) {
+                    f32x16 a1 = {}, a2 = {};
+#pragma unroll
+                    for (int K = 0; K < NB; ++K)
+#pragma unroll
+                        for (int f = 0; f < 2; ++f) {
+                            a1 = mfma32w(XR[I][K][f], XR[J][K][f], a1);
+                            if (J != I) a2 = mfma32w(XR[J][K][f], XR[I][K][f], a2);
+                            if constexpr (SPLIT_X) {
+                                a1 = mfma32w(XR[I][K][f], XL[J][K][f], a1);
+                                a1 = mfma32w(XL[I][K][f], XR[J][K][f], a1);
+                                if (J != I) {
+                                    a2 = mfma32w(XR[J][K][f], XL[I][K][f], a2);
+                                    a2 = mfma32w(XL[J][K][f], XR[I][K][f], a2);
+                                }
+                            }
+                        }
+                    Abf[I][J][0] = cvt8(a1, 0); Abf[I][J][1] = cvt8(a1, 8);
+                    if (J != I) { Abf[J][I][0] = cvt8(a2, 0); Abf[J][I][1] = cvt8(a2, 8); }
+                    if constexpr (SPLIT_A) {
+                        Alo[I][J][0] = cvt8_lo(a1, 0, Abf[I][J][0]); Alo[I][J][1] = cvt8_lo(a1, 8, Abf[I][J][1]);
+                        if (J != I) {
+                            Alo[J][I][0] = cvt8_lo(a2, 0, Abf[J][I][0]); Alo[J][I][1] = cvt8_lo(a2, 8, Abf[J][I][1]);
+                        }
+                    }
+                }
+            __syncthreads();
+        } else {
+            constexpr int NK = TK / 16;
+            u32x4 RF[NB][NK];
+#pragma unroll
+            for (int I = 0; I < NB; ++I)
+#pragma unroll
+                for (int kc = 0; kc < NK; ++kc)
+                    RF[I][kc] = *reinterpret_cast<const u32x4*>(&sX[(I * 32 + l32) * LD + kc * 16 + g * 8]);
+#pragma unroll
+            for (int I = 0; I < NB; ++I)
+#pragma unroll
+                for (int J = I; J < NB; ++J) {
+                    f32x16 a1 = {}, a2 = {};
+#pragma unroll
+                    for (int kc = 0; kc < NK; ++kc) {
+                        a1 = mfma32w(RF[I][kc], RF[J][kc], a1);
+                        if (J != I) a2 = mfma32w(RF[J][kc], RF[I][kc], a2);
+                    }
+                    Abf[I][J][0] = cvt8(a1, 0); Abf[I][J][1] = cvt8(a1, 8);
+                    if (J != I) { Abf[J][I][0] = cvt8(a2, 0); Abf[J][I][1] = cvt8(a2, 8); }
+                }
+        }
+
+        // B = b A + c A^2 (A symmetric: AL(A(K,P)) is the row operand of A(P,K))
+#pragma unroll
+        for (int P = 0; P < NB; ++P)
+#pragma unroll
+            for (int Q = P; Q < NB; ++Q) {
+                f32x16 a1 = {}, a2 = {};
+#pragma unroll
+                for (int K = 0; K < NB; ++K)
+#pragma unroll
+                    for (int f = 0; f < 2; ++f) {
+                        a1 = mfma32w(Abf[K][P][f], Abf[K][Q][f], a1);
+                        if (Q != P) a2 = mfma32w(Abf[K][Q][f], Abf[K][P][f], a2);
+                        if constexpr (SPLIT_A) {
+                            a1 = mfma32w(Abf[K][P][f], Alo[K][Q][f], a1);
+                            a1 = mfma32w(Alo[K][P][f], Abf[K][Q][f], a1);
+                            if (Q != P) {
+                                a2 = mfma32w(Abf[K][Q][f], Alo[K][P][f], a2);
+                                a2 = mfma32w(Alo[K][Q][f], Abf[K][P][f], a2);
+                            }
+                        }
+                    }
+                if (!MASTER32 && Q == P) {
+                    // kernel tile 128 folds a X into the product: B' = a I + B
+#pragma unroll
+                    for (int q = 0; q < 16; ++q)
+                        if ((q >> 2) * 8 + g * 4 + (q & 3) == l32) a1[q] += ca / cc;
+                }
+                // a1 <- b A + c A^2 in place, then rounded (hi, and lo when split)
+#pragma unroll
+                for (int f = 0; f < 2; ++f)
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const int e = 8 * f + 2 * k;
+                        float A0 = lo_f(Abf[P][Q][f][k]), A1 = hi_f(Abf[P][Q][f][k]);
+                        if constexpr (SPLIT_A) { A0 += lo_f(Alo[P][Q][f][k]); A1 += hi_f(Alo[P][Q][f][k]); }
+                        a1[e] = cb * A0 + cc * a1[e];
+                        a1[e + 1] = cb * A1 + cc * a1[e + 1];
+                        if (Q != P) {
+                            float C0 = lo_f(Abf[Q][P][f][k]), C1 = hi_f(Abf[Q][P][f][k]);
+                            if constexpr (SPLIT_A) { C0 += lo_f(Alo[Q][P][f][k]); C1 += hi_f(Alo[Q][P][f][k]); }
+                            a2[e] = cb * C0 + cc * a2[e];
+                            a2[e + 1] = cb * C1 + cc * a2[e + 1];
+                        }
+                    }
+                Bbf[P][Q][0] = cvt8(a1, 0); Bbf[P][Q][1] = cvt8(a1, 8);
+                if (Q != P) { Bbf[Q][P][0] = cvt8(a2, 0); Bbf[Q][P][1] = cvt8(a2, 8); }
+                if constexpr (SPLIT_B) {
+                    Blo[P][Q][0] = cvt8_lo(a1, 0, Bbf[P][Q][0]); Blo[P][Q][1] = cvt8_lo(a1, 8, Bbf[P][Q][1]);
+                    if (Q != P) {
+                        Blo[Q][P][0] = cvt8_lo(a2, 0, Bbf[Q][P][0]); Blo[Q][P][1] = cvt8_lo(a2, 8, Bbf[Q][P][1]);
+                    }
+                }
+            }
+
+        // X' = a X + B X, computed as X'^T blocks so the result lands in RL
+#pragma unroll
+        for (int J = 0; J < NB; ++J) {
+            u32x4 opA[NB][2];
+            u32x4 opL[SPLIT_X ? NB : 1][2];
+#pragma unroll
+            for (int K = 0; K < NB; ++K)
+#pragma unroll
+                for (int f = 0; f < 2; ++f) {
+                    opA[K][f] = tr_frag(sX, K, J, f);
+                    if constexpr (SPLIT_X) opL[K][f] = tr_frag(sXl, K, J, f);
+                }
+            f32x16 acc[NB];
+#pragma unroll
+            for (int I = 0; I < NB; ++I) {
+                if constexpr (MASTER32) acc[I] = Xm[I][J] * ca;
+                else acc[I] = f32x16{};
+            }
+#pragma unroll
+            for (int K = 0; K < NB; ++K)
+#pragma unroll
+                for (int f = 0; f < 2; ++f)
+#pragma unroll
+                    for (int I = 0; I < NB; ++I) {
+                        acc[I] = mfma32w(opA[K][f], Bbf[K][I][f], acc[I]);
+                        if constexpr (SPLIT_B) acc[I] = mfma32w(opA[K][f], Blo[K][I][f], acc[I]);
+                        if constexpr (SPLIT_X) acc[I] = mfma32w(opL[K][f], Bbf[K][I][f], acc[I]);
+                    }
+#pragma unroll
+            for (int I = 0; I < NB; ++I) {
+                if constexpr (MASTER32) {
+                    Xm[I][J] = acc[I];
+                } else {
+                    // column block J of X is no longer read by this step
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        u32x2 v = {pack2(acc[I][4 * m], acc[I][4 * m + 1]), pack2(acc[I][4 * m + 2], acc[I][4 * m + 3])};
+                        *reinterpret_cast<u32x2*>(&sX[rl_off(I, J, m)]) = v;
+                    }
+                }
+            }
+        }
+        __syncthreads();
+    }
+
+    // ---- write back in place (Muon: W <- W - eta X) ----
+    if constexpr (MASTER32) {
+#pragma unroll
+        for (int I = 0; I < NB; ++I)
+#pragma unroll
+            for (int J = 0; J < NB; ++J)
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    u32x2 v = {pack2(Xm[I][J][4 * m], Xm[I][J][4 * m + 1]), pack2(Xm[I][J][4 * m + 2], Xm[I][J][4 * m + 3])};
+                    *reinterpret_cast<u32x2*>(&sX[rl_off(I, J, m)]) = v;
+                }
+        __syncthreads();
+    }
+    {
+        unsigned short* obase = mbase;
+        int64_t old = me.m_ld;
+        bool ovec = mvec;
+        if constexpr (MUON) {
+            obase = reinterpret_cast<unsigned short*>(me.w) + (int64_t)r0 * me.w_ld + c0;
+            old = me.w_ld;
+            ovec = vec_ok(me.w, me.w_ld, c0);
+        }
+#pragma unroll
+        for (int it = 0; it < IO::NCH; ++it) {
+            const int idx = it * 64 + lane;
+            const int r = idx / IO::CPR, col = (idx % IO::CPR) * 8;
+            u16x8 v = *reinterpret_cast<const u16x8*>(&sX[r * LD + col]);
+            if constexpr (MUON) {
+                u16x8 wv = IO::load(obase, old, r, col, h, w, ovec);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] = f2bf(bf2f(wv[e]) - args.eta * bf2f(v[e]));
+            }
+            IO::store(obase, old, r, col, h, w, ovec, v);
+        }
+    }
+}
+
+template <int TK, bool MUON, bool PRECISE>
+static hipError_t launch_tk(const ResidentArgs& a, hipStream_t s) {
+    if (a.total_tiles <= 0) return hipSuccess;
+    hipLaunchKernelGGL((resident_kernel<TK, MUON, PRECISE>), dim3(a.total_tiles), dim3(64), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_resident(const ResidentArgs& a, int kernel_tile, bool muon, bool precise, hipStream_t s) {
+    if (precise) {
+        switch (kernel_tile) {
+            case 32: return muon ? launch_tk<32, true, true>(a, s) : launch_tk<32, false, true>(a, s);
+            case 64: return muon ? launch_tk<64, true, true>(a, s) : launch_tk<64, false, true>(a, s);
+            default: return hipErrorInvalidValue;
+        }
+    }
+    switch (kernel_tile) {
+        case 32: return muon ? launch_tk<32, true, false>(a, s) : launch_tk<32, false, false>(a, s);
+        case 64: return muon ? launch_tk<64, true, false>(a, s) : launch_tk<64, false, false>(a, s);
+        case 128: return muon ? launch_tk<128, true, false>(a, s) : launch_tk<128, false, false>(a, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace himuon

@@ -1,0 +1,499 @@
+// Step-by-step tiled Newton-Schulz on gfx950: tile sizes above 128, fp32
+// data, and the full-matrix map (T >= max(rows, cols)).
+//
+// The map per tile is Algorithm 1 of the "Gram Newton-Schulz" summary page
+// (section 3): normalise by ||X||_F + eps, orient so the Gram matrix is the
+// short side, then K steps of A = X X^T, B = b A + c A^2, X = a X + B X.  Each
+// step is three batched launches over the chunk's tiles, all on MFMA:
+//   gram : A  = X X^T            lower 128x128 blocks, stored with their mirror
+//   poly : B' = a I + b A + c A A lower blocks (A symmetric, so A A = A A^T)
+//   apply: X' = B' X             (equal to a X + B X in exact arithmetic)
+// The last apply writes the result in place in the input dtype, undoing the
+// orientation.  Two small launches before the steps take the per-tile sum of
+// squares (fixed partition and order, so the result is deterministic) and
+// write the normalised, oriented tiles.
+//
+// Workgroup -> (tile, block) ids are remapped so that the blocks of one tile
+// run on one XCD and share its L2.
+
+#include "common.h"
+
+namespace himuon {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+
+#define LDS_AS __attribute__((address_space(3)))
+
+namespace {
+
+__device__ __forceinline__ float bf2f(unsigned short u) { return __uint_as_float(((unsigned)u) << 16); }
+__device__ __forceinline__ unsigned short f2bf(float f) {
+    __bf16 b = (__bf16)f;
+    return __builtin_bit_cast(unsigned short, b);
+}
+
+// Element access for the two storage types.
+template <int DT> struct Elem;
+template <> struct Elem<0> {
+    using T = unsigned short;
+    __device__ static float ld(const T* p) { return bf2f(*p); }
+    __device__ static T cv(float f) { return f2bf(f); }
+};
+template <> struct Elem<1> {
+    using T = float;
+    __device__ static float ld(const T* p) { return *p; }
+    __device__ static T cv(float f) { return f; }
+};
+
+struct TileRef {
+    TileGeom g;
+    int32_t mi;
+};
+
+__device__ __forceinline__ TileRef find_tile(const StepArgs& a, int t) {
+    int mi = 0;
+    for (int i = 1; i < a.nmats; ++i)
+        if (t >= a.mats[i].tile_base) mi = i;
+    const MatEntry& me = a.mats[mi];
+    TileRef r;
+    r.mi = mi;
+    r.g = class_tile(me, a.T, t - me.tile_base);
+    r.g.xoff -= a.xbase;
+    r.g.aoff -= a.abase;
+    return r;
+}
+
+__device__ __forceinline__ float block_sum(float v, float* red) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+    const int wave = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) red[wave] = v;
+    __syncthreads();
+    float s = 0.f;
+    for (int i = 0; i < (int)(blockDim.x >> 6); ++i) s += red[i];
+    __syncthreads();
+    return s;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Normalisation.  Grid: wg_norm workgroups per tile; workgroup k of a tile
+// handles the tile's 64x64 sub-blocks k, k + wg_norm, ...
+// Pass 0 (partial): Muon prologue M <- mu M + G (stored), partial sum of squares.
+// Pass 1 (write): scale = 1 / (sqrt(sum of the tile's partials) + eps); write
+// the scaled tile oriented into Xc, or, when K == 0, straight back in place.
+// ---------------------------------------------------------------------------
+template <int IO, int WK, int PASS>
+__global__ __launch_bounds__(256) void step_norm_kernel(const StepArgs a) {
+    using E = Elem<IO>;
+    using ET = typename E::T;
+    using EW = Elem<WK>;
+    using WT = typename EW::T;
+    __shared__ float red[4];
+    __shared__ float tileT[64][65];
+
+    const int tl = blockIdx.x / a.wg_norm, k = blockIdx.x % a.wg_norm;
+    const int t = a.tile_begin + tl;
+    if (t >= a.tile_end) return;
+    const TileRef tr = find_tile(a, t);
+    const TileGeom& g = tr.g;
+    const MatEntry& me = a.mats[tr.mi];
+    ET* mbase = reinterpret_cast<ET*>(me.m) + (int64_t)g.r0 * me.m_ld + g.c0;
+    const int sbw = (g.w + 63) / 64, sbh = (g.h + 63) / 64;
+    const int tid = threadIdx.x;
+
+    if (PASS == 0) {
+        const ET* gbase = a.muon ? reinterpret_cast<const ET*>(me.g) + (int64_t)g.r0 * me.g_ld + g.c0 : nullptr;
+        float ss = 0.f;
+        for (int sb = k; sb < sbw * sbh; sb += a.wg_norm) {
+            const int i0 = (sb / sbw) * 64, j0 = (sb % sbw) * 64;
+            for (int e = tid; e < 64 * 64; e += 256) {
+                const int i = i0 + e / 64, j = j0 + e % 64;
+                if (i < g.h && j < g.w) {
+                    ET* p = mbase + (int64_t)i * me.m_ld + j;
+                    float x = E::ld(p);
+                    if (a.muon) {
+                        ET nv = E::cv(a.mu * x + E::ld(gbase + (int64_t)i * me.g_ld + j));
+                        *p = nv;
+                        x = E::ld(&nv);
+                    }
+                    ss += x * x;
+                }
+            }
+        }
+        ss = block_sum(ss, red);
+        if (tid == 0) a.partial[(int64_t)tl * a.wg_norm + k] = ss;
+        return;
+    }
+
+    float tot = 0.f;
+    for (int i = 0; i < a.wg_norm; ++i) tot += a.partial[(int64_t)tl * a.wg_norm + i];
+    const float scale = 1.0f / (sqrtf(tot) + a.eps);
+    WT* xo = reinterpret_cast<WT*>(a.Xc) + g.xoff;
+    const int64_t xld = round8(g.s);
+    for (int sb = k; sb < sbw * sbh; sb += a.wg_norm) {
+        const int i0 = (sb / sbw) * 64, j0 = (sb % sbw) * 64;
+        if (a.K == 0) {
+            // output = normalised tile, in place (Muon: W -= eta * it)
+            ET* wbase = a.muon ? reinterpret_cast<ET*>(me.w) + (int64_t)g.r0 * me.w_ld + g.c0 : nullptr;
+            for (int e = tid; e < 64 * 64; e += 256) {
+                const int i = i0 + e / 64, j = j0 + e % 64;
+                if (i < g.h && j < g.w) {
+                    const float y = E::ld(mbase + (int64_t)i * me.m_ld + j) * scale;
+                    if (a.muon) {
+                        ET* wp = wbase + (int64_t)i * me.w_ld + j;
+                        *wp = E::cv(E::ld(wp) - a.eta * y);
+                    } else {
+                        mbase[(int64_t)i * me.m_ld + j] = E::cv(y);
+                    }
+                }
+            }
+            continue;
+        }
+        if (!g.tr) {
+            for (int e = tid; e < 64 * 64; e += 256) {
+                const int i = i0 + e / 64, j = j0 + e % 64;
+                if (i < g.h && j < g.w) xo[(int64_t)i * xld + j] = EW::cv(E::ld(mbase + (int64_t)i * me.m_ld + j) * scale);
+            }
+        } else {
+            // tall tile: stored transposed, through LDS so both sides coalesce
+            for (int e = tid; e < 64 * 64; e += 256) {
+                const int i = e / 64, j = e % 64;
+                float v = 0.f;
+                if (i0 + i < g.h && j0 + j < g.w) v = E::ld(mbase + (int64_t)(i0 + i) * me.m_ld + j0 + j) * scale;
+                tileT[i][j] = v;
+            }
+            __syncthreads();
+            for (int e = tid; e < 64 * 64; e += 256) {
+                const int j = e / 64, i = e % 64;   // oriented row j (original column), column i
+                if (i0 + i < g.h && j0 + j < g.w) xo[(int64_t)(j0 + j) * xld + i0 + i] = EW::cv(tileT[i][j]);
+            }
+            __syncthreads();
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Batched MFMA GEMM over the chunk's tiles.  128x128 output block per
+// workgroup of 4 waves (2x2, 64x64 each as 2x2 blocks of 32x32).
+// MODE 0 gram:  C = X X^T          (r x r, contraction over s), lower blocks
+// MODE 1 poly:  C = A A, B' = a I + b A + c C                   lower blocks
+// MODE 2 apply: C = B' X           (r x s, contraction over r)
+// bf16: v_mfma_f32_32x32x16_bf16, k chunk 32; fp32: v_mfma_f32_32x32x2f32,
+// k chunk 16.  Row operands are read from LDS along k; the X operand of apply
+// (k along rows of X) uses ds_read_tr16_b64 for bf16.
+// ---------------------------------------------------------------------------
+// Final result element (i, j) of a tile, in place in the matrix dtype (Muon:
+// W <- W - eta * result, with the result rounded to the dtype first, as the
+// plain map would store it).
+template <int IO>
+__device__ __forceinline__ void store_out(const StepArgs& a, const MatEntry& me, const TileGeom& g, int oi, int oj,
+                                          float v) {
+    using E = Elem<IO>;
+    using ET = typename E::T;
+    const ET rv = E::cv(v);
+    if (a.muon) {
+        ET* wp = reinterpret_cast<ET*>(me.w) + (int64_t)(g.r0 + oi) * me.w_ld + g.c0 + oj;
+        *wp = E::cv(E::ld(wp) - a.eta * E::ld(&rv));
+    } else {
+        ET* op = reinterpret_cast<ET*>(me.m) + (int64_t)(g.r0 + oi) * me.m_ld + g.c0 + oj;
+        *op = rv;
+    }
+}
+
+template <int DT> struct GemmCfg;
+template <> struct GemmCfg<0> {
+    static constexpr int BK = 32, EPC = 8;         // k chunk, elements per 16-byte chunk
+    static constexpr int LDP = BK + 8;             // row-panel stride (elements)
+    static constexpr int LDN = 128 + 16;           // X-panel stride for apply
+};
+template <> struct GemmCfg<1> {
+    static constexpr int BK = 16, EPC = 4;
+    static constexpr int LDP = BK + 1;
+    static constexpr int LDN = 128 + 4;
+};
+
+template <int DT, int MODE>
+__global__ __launch_bounds__(256) void step_gemm_kernel(const StepArgs a) {
+    using E = Elem<DT>;           // workspace element
+    using ET = typename E::T;
+    using C = GemmCfg<DT>;
+    constexpr int BK = C::BK, EPC = C::EPC, LDP = C::LDP, LDN = C::LDN;
+    constexpr bool NN = MODE == 2;
+    __shared__ __attribute__((aligned(16))) ET sP[128 * LDP];
+    __shared__ __attribute__((aligned(16))) ET sQ[NN ? BK * LDN : 128 * LDP];
+
+    // ---- workgroup -> (tile, block), blocks of one tile on one XCD ----
+    const int nwg = a.grid_blocks;
+    const int L = (blockIdx.x & 7) * (nwg >> 3) + (blockIdx.x >> 3);
+    const int bpt = NN ? a.nb_max * a.ns_max : a.nb_max * (a.nb_max + 1) / 2;
+    const int tl = L / bpt, b = L - tl * bpt;
+    const int t = a.tile_begin + tl;
+    if (t >= a.tile_end) return;
+    const TileRef tref = find_tile(a, t);
+    const TileGeom& g = tref.g;
+    const int nb = (g.r + 127) / 128, ns = (g.s + 127) / 128;
+    int bm, bn;
+    if (NN) {
+        bm = b / a.ns_max;
+        bn = b - bm * a.ns_max;
+        if (bm >= nb || bn >= ns) return;
+    } else {
+        bm = (int)((sqrtf(8.f * b + 1.f) - 1.f) * 0.5f);
+        while ((bm + 1) * (bm + 2) / 2 <= b) ++bm;
+        while (bm * (bm + 1) / 2 > b) --bm;
+        bn = b - bm * (bm + 1) / 2;
+        if (bm >= nb) return;
+    }
+    const int m0 = bm * 128, n0 = bn * 128;
+
+    // operands: P (rows m0.., k contiguous), Q (NT: rows n0.., k contiguous;
+    // NN: rows k.., columns n0..)
+    const ET* P;
+    const ET* Q;
+    int64_t ldp, ldq;
+    int prow, kdim, qrow, qcol;
+    if (MODE == 0) {
+        P = reinterpret_cast<const ET*>(a.Xc) + g.xoff; ldp = round8(g.s);
+        Q = P; ldq = ldp;
+        prow = g.r; kdim = g.s; qrow = g.r; qcol = 0;
+    } else if (MODE == 1) {
+        P = reinterpret_cast<const ET*>(a.A) + g.aoff; ldp = round8(g.r);
+        Q = P; ldq = ldp;
+        prow = g.r; kdim = g.r; qrow = g.r; qcol = 0;
+    } else {
+        P = reinterpret_cast<const ET*>(a.B) + g.aoff; ldp = round8(g.r);
+        Q = reinterpret_cast<const ET*>(a.Xc) + g.xoff; ldq = round8(g.s);
+        prow = g.r; kdim = g.r; qrow = g.r; qcol = g.s;
+    }
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int l32 = lane & 31, gl = lane >> 5;
+
+    // global -> register staging: 2 chunks of 16 bytes per panel per thread
+    u32x4 rp[2], rq[2];
+    auto load_panels = [&](int k0) {
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            const int c = tid + 256 * p;
+            {   // P: 128 rows x BK
+                const int row = c / (BK / EPC), kc = (c % (BK / EPC)) * EPC;
+                u32x4 v = {0, 0, 0, 0};
+                const int gr = m0 + row, gk = k0 + kc;
+                if (gr < prow && gk < kdim) {
+                    v = *reinterpret_cast<const u32x4*>(P + (int64_t)gr * ldp + gk);
+                    if (gk + EPC > kdim) {
+                        ET* e = reinterpret_cast<ET*>(&v);
+#pragma unroll
+                        for (int q = 0; q < EPC; ++q) if (gk + q >= kdim) e[q] = ET(0);
+                    }
+                }
+                rp[p] = v;
+            }
+            if (!NN) {
+                const int row = c / (BK / EPC), kc = (c % (BK / EPC)) * EPC;
+                u32x4 v = {0, 0, 0, 0};
+                const int gr = n0 + row, gk = k0 + kc;
+                if (gr < qrow && gk < kdim) {
+                    v = *reinterpret_cast<const u32x4*>(Q + (int64_t)gr * ldq + gk);
+                    if (gk + EPC > kdim) {
+                        ET* e = reinterpret_cast<ET*>(&v);
+#pragma unroll
+                        for (int q = 0; q < EPC; ++q) if (gk + q >= kdim) e[q] = ET(0);
+                    }
+                }
+                rq[p] = v;
+            } else {
+                constexpr int CPR = 128 / EPC;
+                const int row = c / CPR, cc = (c % CPR) * EPC;
+                u32x4 v = {0, 0, 0, 0};
+                const int gk = k0 + row, gc = n0 + cc;
+                if (gk < kdim && gc < qcol) {
+                    v = *reinterpret_cast<const u32x4*>(Q + (int64_t)gk * ldq + gc);
+                    if (gc + EPC > qcol) {
+                        ET* e = reinterpret_cast<ET*>(&v);
+#pragma unroll
+                        for (int q = 0; q < EPC; ++q) if (gc + q >= qcol) e[q] = ET(0);
+                    }
+                }
+                rq[p] = v;
+            }
+        }
+    };
+    auto store_panels = [&]() {
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            const int c = tid + 256 * p;
+            const int row = c / (BK / EPC), kc = (c % (BK / EPC)) * EPC;
+            if (DT == 0) {
+                *reinterpret_cast<u32x4*>(&sP[row * LDP + kc]) = rp[p];
+            } else {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) reinterpret_cast<unsigned*>(sP)[row * LDP + kc + q] = rp[p][q];
+            }
+            if (!NN) {
+                if (DT == 0) {
+                    *reinterpret_cast<u32x4*>(&sQ[row * LDP + kc]) = rq[p];
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) reinterpret_cast<unsigned*>(sQ)[row * LDP + kc + q] = rq[p][q];
+                }
+            } else {
+                constexpr int CPR = 128 / EPC;
+                const int nrow = c / CPR, cc = (c % CPR) * EPC;
+                *reinterpret_cast<u32x4*>(&sQ[nrow * LDN + cc]) = rq[p];
+            }
+        }
+    };
+
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+
+    load_panels(0);
+    for (int k0 = 0; k0 < kdim; k0 += BK) {
+        __syncthreads();
+        store_panels();
+        __syncthreads();
+        if (k0 + BK < kdim) load_panels(k0 + BK);
+        if constexpr (DT == 0) {
+#pragma unroll
+            for (int kk = 0; kk < BK / 16; ++kk) {
+                bf16x8 av[2], bv[2];
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+                    av[i] = *reinterpret_cast<const bf16x8*>(&sP[(wm * 64 + i * 32 + l32) * LDP + kk * 16 + gl * 8]);
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    if (!NN) {
+                        bv[j] = *reinterpret_cast<const bf16x8*>(&sQ[(wn * 64 + j * 32 + l32) * LDP + kk * 16 + gl * 8]);
+                    } else {
+                        const int G = lane >> 4, i16 = lane & 15;
+                        const int col = wn * 64 + j * 32 + 16 * (G & 1) + 4 * (i16 & 3);
+                        const int row = kk * 16 + 8 * gl + (i16 >> 2);
+                        bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(&sQ[row * LDN + col]));
+                        bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(&sQ[(row + 4) * LDN + col]));
+                        bv[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
+            }
+        } else {
+            const float* fP = reinterpret_cast<const float*>(sP);
+            const float* fQ = reinterpret_cast<const float*>(sQ);
+#pragma unroll
+            for (int kk = 0; kk < BK / 2; ++kk) {
+                float av[2], bv[2];
+#pragma unroll
+                for (int i = 0; i < 2; ++i) av[i] = fP[(wm * 64 + i * 32 + l32) * LDP + kk * 2 + gl];
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    bv[j] = NN ? fQ[(kk * 2 + gl) * LDN + wn * 64 + j * 32 + l32]
+                               : fQ[(wn * 64 + j * 32 + l32) * LDP + kk * 2 + gl];
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[i], bv[j], acc[i][j], 0, 0, 0);
+            }
+        }
+    }
+
+    // ---- epilogue: lane l, register q of block (i,j) holds
+    //      C[m0 + wm*64 + i*32 + rho(l,q)][n0 + wn*64 + j*32 + l%32] ----
+    const float ca = a.abc[3 * a.step], cb = a.abc[3 * a.step + 1], cc = a.abc[3 * a.step + 2];
+    const bool last = (MODE == 2) && (a.step == a.K - 1);
+    const MatEntry& me = a.mats[tref.mi];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const int row = m0 + wm * 64 + i * 32 + (q >> 2) * 8 + gl * 4 + (q & 3);
+                const int col = n0 + wn * 64 + j * 32 + l32;
+                float v = acc[i][j][q];
+                if (MODE == 0) {
+                    if (row < g.r && col < g.r) {
+                        ET* Ao = reinterpret_cast<ET*>(a.A) + g.aoff;
+                        const int64_t ld = round8(g.r);
+                        const ET e = E::cv(v);
+                        Ao[(int64_t)row * ld + col] = e;
+                        if (bm != bn) Ao[(int64_t)col * ld + row] = e;
+                    }
+                } else if (MODE == 1) {
+                    if (row < g.r && col < g.r) {
+                        const ET* Ai = reinterpret_cast<const ET*>(a.A) + g.aoff;
+                        ET* Bo = reinterpret_cast<ET*>(a.B) + g.aoff;
+                        const int64_t ld = round8(g.r);
+                        float bv = cb * E::ld(Ai + (int64_t)row * ld + col) + cc * v;
+                        if (row == col) bv += ca;
+                        const ET e = E::cv(bv);
+                        Bo[(int64_t)row * ld + col] = e;
+                        if (bm != bn) Bo[(int64_t)col * ld + row] = e;
+                    }
+                } else {
+                    if (row < g.r && col < g.s) {
+                        if (!last) {
+                            ET* Xo = reinterpret_cast<ET*>(a.Xn) + g.xoff;
+                            Xo[(int64_t)row * round8(g.s) + col] = E::cv(v);
+                        } else {
+                            const int oi = g.tr ? col : row, oj = g.tr ? row : col;
+                            if (a.io_dtype == 0) store_out<0>(a, me, g, oi, oj, v);
+                            else store_out<1>(a, me, g, oi, oj, v);
+                        }
+                    }
+                }
+            }
+}
+
+template <int IO, int WK, int PASS>
+static hipError_t launch_norm_dt(const StepArgs& a, hipStream_t s) {
+    const int n = (a.tile_end - a.tile_begin) * a.wg_norm;
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL((step_norm_kernel<IO, WK, PASS>), dim3(n), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+template <int PASS>
+static hipError_t launch_norm_pass(const StepArgs& a, hipStream_t s) {
+    if (a.io_dtype == 0) return a.wk_dtype == 0 ? launch_norm_dt<0, 0, PASS>(a, s) : launch_norm_dt<0, 1, PASS>(a, s);
+    return launch_norm_dt<1, 1, PASS>(a, s);
+}
+
+hipError_t launch_step_norm(const StepArgs& a, hipStream_t s) {
+    hipError_t e = launch_norm_pass<0>(a, s);
+    if (e != hipSuccess) return e;
+    return launch_norm_pass<1>(a, s);
+}
+
+template <int MODE>
+static hipError_t launch_gemm(const StepArgs& a, hipStream_t s) {
+    if (a.grid_blocks <= 0) return hipSuccess;
+    if (a.wk_dtype == 0)
+        hipLaunchKernelGGL((step_gemm_kernel<0, MODE>), dim3(a.grid_blocks), dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL((step_gemm_kernel<1, MODE>), dim3(a.grid_blocks), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_step_gram(const StepArgs& a, hipStream_t s) { return launch_gemm<0>(a, s); }
+hipError_t launch_step_poly(const StepArgs& a, hipStream_t s) { return launch_gemm<1>(a, s); }
+hipError_t launch_step_apply(const StepArgs& a, hipStream_t s) { return launch_gemm<2>(a, s); }
+
+}  // namespace himuon
