@@ -91,6 +91,9 @@ def main():
     ap.add_argument("--K", type=int, default=5)
     ap.add_argument("--cap", type=int, default=None, help="workspace cap in bytes")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many MiB, 5 times (used to "
+                         "calibrate the HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -99,6 +102,16 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_mib:
+        n = args.copy_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "copies": 5}), flush=True)
+        return
 
     import tiled_newton_schulz_amd as H
     import workloads

@@ -20,7 +20,11 @@ QUINTIC_COEFFS = (3.4445, -4.7750, 2.0315)
 
 def _coeff_list(coeffs, K=None):
     """Normalise coefficients to a list of K (a, b, c) triples."""
+    if K == 0:
+        return []
     arr = np.asarray(coeffs, dtype=np.float64)
+    if arr.size == 0 and K is None:
+        return []
     if arr.ndim == 1:
         if arr.shape[0] != 3:
             raise ValueError("a single coefficient triple must have 3 entries")

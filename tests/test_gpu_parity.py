@@ -135,10 +135,11 @@ def test_zero_and_tiny_tiles(cuda):
     for dt in ("bf16", "fp32"):
         for T in (64, 256):
             x = torch.zeros(300, 200, dtype=torch.bfloat16 if dt == "bf16" else torch.float32)
-            x[:T, :T] = workloads.round_to(np.random.default_rng(3).standard_normal((T, T)) * 1e-3, dt)
+            tw = min(T, 200)
+            x[:T, :tw] = workloads.round_to(np.random.default_rng(3).standard_normal((T, tw)) * 1e-3, dt)
             err, g = full_check(x, T, dt)
             assert err <= TOL[dt]
-            assert torch.count_nonzero(g[T:, :]) == 0 and torch.count_nonzero(g[:, T:]) == 0
+            assert torch.count_nonzero(g[T:, :]) == 0 and torch.count_nonzero(g[:, tw:]) == 0
 
 
 # ------------------------------------------------------------- invariants
@@ -219,11 +220,13 @@ def test_muon_step(cuda, dt, T, K):
     Wg, Mg, Gg = W.cuda(), M.cuda(), G.cuda()
     H.himuon_muon_step([Wg], [Mg], [Gg], T, K, COEFFS, mu=mu, eta=eta)
     torch.cuda.synchronize()
-    # momentum: mu M + G rounded once to the dtype (one ulp allows for the
-    # fp32-versus-fp64 evaluation before the rounding)
-    m_new = workloads.round_to(mu * M.double().numpy() + G.double().numpy(), dt).double()
-    ulp = m_new.abs() * (2.0 ** -7 if dt == "bf16" else 2.0 ** -23)
-    assert bool(((Mg.cpu().double() - m_new).abs() <= ulp).all()), "momentum differs by more than one ulp"
+    # momentum: mu M + G rounded once to the dtype; the device evaluates the sum
+    # in fp32, so allow one ulp of the result plus the fp32 evaluation error
+    # (which matters where mu M and G nearly cancel)
+    mM, gG = mu * M.double(), G.double()
+    m_new = workloads.round_to((mM + gG).numpy(), dt).double()
+    bound = m_new.abs() * (2.0 ** -7 if dt == "bf16" else 2.0 ** -23) + 2.0 ** -22 * (mM.abs() + gG.abs())
+    assert bool(((Mg.cpu().double() - m_new).abs() <= bound).all()), "momentum differs beyond rounding"
     # weights: W - eta * tiledNS(M) with M as stored; per tile the difference
     # is bounded by W's own rounding plus eta times the map's tolerance
     U = oracle.tiled_ns(Mg.cpu().double().numpy(), T, COEFFS, K=K)

@@ -23,10 +23,13 @@ SOURCES = ["resident.hip", "stepwise.hip", "api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
-# Packed fp32 VALU ops are kept out of generated code (see DESIGN notes on the
-# target); the host pass warns that it does not know the feature.
+# Packed fp32 VALU ops are kept out of generated code; the host pass warns
+# that it does not know the feature.  MFMA results are kept in VGPRs (rather
+# than AGPRs) so that converting an accumulator block to a bf16 operand needs
+# no AGPR-to-VGPR copies.
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-mllvm", "-amdgpu-mfma-vgpr-form=1",
           "-I", INCLUDE, "-I", CSRC]
 
 
