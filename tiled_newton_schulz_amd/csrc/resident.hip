@@ -143,6 +143,13 @@ __global__ __launch_bounds__(64) void resident_kernel(const ResidentArgs args) {
 
     __shared__ __attribute__((aligned(16))) unsigned short sX[TK * LD];
     __shared__ __attribute__((aligned(16))) unsigned short sXl[SPLIT_X ? TK * LD : 8];
+    // Kernel tile 128 computes only the lower 32x32 blocks of the symmetric
+    // products A and A^2; an upper block is the transpose of a lower one and is
+    // made by staging the lower block in LDS as its transpose and reading it
+    // back with ds_read_tr16_b64.
+    constexpr bool SYM = !MASTER32;
+    constexpr int LDT = 40;   // staging row stride (elements)
+    __shared__ __attribute__((aligned(16))) unsigned short sT[SYM ? 2 * 32 * LDT : 8];
 
     const int lane = threadIdx.x;
     const int l32 = lane & 31;
@@ -206,6 +213,26 @@ __global__ __launch_bounds__(64) void resident_kernel(const ResidentArgs args) {
         bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(&buf[rowb * LD + col]));
         bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(&buf[(rowb + 8) * LD + col]));
         return __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    // Transpose of a 32x32 block held in AL: write it into staging slot `slot`
+    // as its transpose, row-major (lane l writes row l%32), then read the AL of
+    // the stored matrix, which is AL of the transpose.
+    auto transpose_al = [&](int slot, const u32x4 (&in)[2], u32x4 (&out)[2]) {
+        unsigned short* buf = &sT[slot * 32 * LDT];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            u32x2 v = {in[m >> 1][2 * (m & 1)], in[m >> 1][2 * (m & 1) + 1]};
+            *reinterpret_cast<u32x2*>(&buf[l32 * LDT + 8 * m + 4 * g]) = v;
+        }
+        const int G = lane >> 4, i16 = lane & 15;
+        const int col = 16 * (G & 1) + 4 * (i16 & 3);
+#pragma unroll
+        for (int f = 0; f < 2; ++f) {
+            const int rowb = 16 * f + 4 * g + (i16 >> 2);
+            bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(&buf[rowb * LDT + col]));
+            bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(&buf[(rowb + 8) * LDT + col]));
+            out[f] = __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
     };
 
     f32x16 Xm[MASTER32 ? NB : 1][MASTER32 ? NB : 1];
@@ -305,22 +332,88 @@ __global__ __launch_bounds__(64) void resident_kernel(const ResidentArgs args) {
 #pragma unroll
                 for (int kc = 0; kc < NK; ++kc)
                     RF[I][kc] = *reinterpret_cast<const u32x4*>(&sX[(I * 32 + l32) * LD + kc * 16 + g * 8]);
+            // lower blocks (I >= J), two accumulator chains at a time
+            constexpr int NL = NB * (NB + 1) / 2;
 #pragma unroll
-            for (int I = 0; I < NB; ++I)
+            for (int p = 0; p < NL; p += 2) {
+                int I1 = 0, J1 = 0, I2 = 0, J2 = 0;
+                {
+                    int c = 0;
 #pragma unroll
-                for (int J = I; J < NB; ++J) {
-                    f32x16 a1 = {}, a2 = {};
+                    for (int i = 0; i < NB; ++i)
 #pragma unroll
-                    for (int kc = 0; kc < NK; ++kc) {
-                        a1 = mfma32w(RF[I][kc], RF[J][kc], a1);
-                        if (J != I) a2 = mfma32w(RF[J][kc], RF[I][kc], a2);
-                    }
-                    Abf[I][J][0] = cvt8(a1, 0); Abf[I][J][1] = cvt8(a1, 8);
-                    if (J != I) { Abf[J][I][0] = cvt8(a2, 0); Abf[J][I][1] = cvt8(a2, 8); }
+                        for (int j = 0; j <= i; ++j) {
+                            if (c == p) { I1 = i; J1 = j; }
+                            if (c == p + 1) { I2 = i; J2 = j; }
+                            ++c;
+                        }
                 }
+                const bool two = p + 1 < NL;
+                f32x16 a1 = {}, a2 = {};
+#pragma unroll
+                for (int kc = 0; kc < NK; ++kc) {
+                    a1 = mfma32w(RF[I1][kc], RF[J1][kc], a1);
+                    if (two) a2 = mfma32w(RF[I2][kc], RF[J2][kc], a2);
+                }
+                Abf[I1][J1][0] = cvt8(a1, 0); Abf[I1][J1][1] = cvt8(a1, 8);
+                if (two) { Abf[I2][J2][0] = cvt8(a2, 0); Abf[I2][J2][1] = cvt8(a2, 8); }
+                if (I1 != J1) transpose_al(0, Abf[I1][J1], Abf[J1][I1]);
+                if (two && I2 != J2) transpose_al(1, Abf[I2][J2], Abf[J2][I2]);
+            }
         }
 
         // B = b A + c A^2 (A symmetric: AL(A(K,P)) is the row operand of A(P,K))
+        if constexpr (SYM) {
+            // lower blocks (P >= Q), two chains at a time; the kernel tile 128
+            // path folds a X into the product: B' = a I + B
+            constexpr int NL = NB * (NB + 1) / 2;
+#pragma unroll
+            for (int p = 0; p < NL; p += 2) {
+                int P1 = 0, Q1 = 0, P2 = 0, Q2 = 0;
+                {
+                    int c = 0;
+#pragma unroll
+                    for (int i = 0; i < NB; ++i)
+#pragma unroll
+                        for (int j = 0; j <= i; ++j) {
+                            if (c == p) { P1 = i; Q1 = j; }
+                            if (c == p + 1) { P2 = i; Q2 = j; }
+                            ++c;
+                        }
+                }
+                const bool two = p + 1 < NL;
+                f32x16 a1 = {}, a2 = {};
+#pragma unroll
+                for (int K = 0; K < NB; ++K)
+#pragma unroll
+                    for (int f = 0; f < 2; ++f) {
+                        a1 = mfma32w(Abf[K][P1][f], Abf[K][Q1][f], a1);
+                        if (two) a2 = mfma32w(Abf[K][P2][f], Abf[K][Q2][f], a2);
+                    }
+#pragma unroll
+                for (int q = 0; q < 16; ++q) {
+                    const bool diag = (q >> 2) * 8 + g * 4 + (q & 3) == l32;
+                    if (P1 == Q1 && diag) a1[q] += ca / cc;
+                    if (two && P2 == Q2 && diag) a2[q] += ca / cc;
+                }
+#pragma unroll
+                for (int f = 0; f < 2; ++f)
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const int e = 8 * f + 2 * k;
+                        a1[e] = cb * lo_f(Abf[P1][Q1][f][k]) + cc * a1[e];
+                        a1[e + 1] = cb * hi_f(Abf[P1][Q1][f][k]) + cc * a1[e + 1];
+                        if (two) {
+                            a2[e] = cb * lo_f(Abf[P2][Q2][f][k]) + cc * a2[e];
+                            a2[e + 1] = cb * hi_f(Abf[P2][Q2][f][k]) + cc * a2[e + 1];
+                        }
+                    }
+                Bbf[P1][Q1][0] = cvt8(a1, 0); Bbf[P1][Q1][1] = cvt8(a1, 8);
+                if (two) { Bbf[P2][Q2][0] = cvt8(a2, 0); Bbf[P2][Q2][1] = cvt8(a2, 8); }
+                if (P1 != Q1) transpose_al(0, Bbf[P1][Q1], Bbf[Q1][P1]);
+                if (two && P2 != Q2) transpose_al(1, Bbf[P2][Q2], Bbf[Q2][P2]);
+            }
+        } else {
 #pragma unroll
         for (int P = 0; P < NB; ++P)
 #pragma unroll
@@ -341,12 +434,6 @@ __global__ __launch_bounds__(64) void resident_kernel(const ResidentArgs args) {
                             }
                         }
                     }
-                if (!MASTER32 && Q == P) {
-                    // kernel tile 128 folds a X into the product: B' = a I + B
-#pragma unroll
-                    for (int q = 0; q < 16; ++q)
-                        if ((q >> 2) * 8 + g * 4 + (q & 3) == l32) a1[q] += ca / cc;
-                }
                 // a1 <- b A + c A^2 in place, then rounded (hi, and lo when split)
 #pragma unroll
                 for (int f = 0; f < 2; ++f)
@@ -373,6 +460,7 @@ __global__ __launch_bounds__(64) void resident_kernel(const ResidentArgs args) {
                     }
                 }
             }
+        }
 
         // X' = a X + B X, computed as X'^T blocks so the result lands in RL
 #pragma unroll
