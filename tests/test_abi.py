@@ -139,7 +139,7 @@ def test_plan_cross_layer_groups():
         p += 200 << 20
     info = H.himuon_plan(many, 128, 5, H.BF16)
     assert info["tiles"] == 24 * 3136
-    assert info["resident_launches"] == math.ceil(168 / 32)
+    assert info["resident_launches"] == math.ceil(168 / 256)
 
 
 def test_plan_moe_ragged_and_chunking():
@@ -153,8 +153,8 @@ def test_plan_moe_ragged_and_chunking():
     info = H.himuon_plan(descs, 256, 5, H.BF16, full)
     # 10,240 full tiles and 2,048 ragged 256x128 / 128x256 edge tiles
     assert info["tiles"] == 64 * 2 * 16 * 6
-    # two tile classes per matrix (interior and one edge), 32 classes per group
-    assert info["chunks"] == math.ceil(2 * len(descs) / 32)
+    # two tile classes per matrix (interior and one edge), 256 classes per group
+    assert info["chunks"] == math.ceil(2 * len(descs) / 256)
     # a small cap forces many chunks, each within the cap
     cap = 64 << 20
     info2 = H.himuon_plan(descs, 256, 5, H.BF16, cap)

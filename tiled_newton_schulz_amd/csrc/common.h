@@ -7,7 +7,7 @@
 namespace himuon {
 
 constexpr int kMaxSteps = 16;     // largest K (matches HIMUON_MAX_STEPS)
-constexpr int kGroup = 32;        // tile classes per launch (kernel-argument table)
+constexpr int kGroup = 256;       // tile classes per launch (kernel-argument table, ~25 KB)
 
 // One tile class of one matrix in a launch: a rectangular block of the
 // matrix's tile grid whose tiles all have the same size th x tw (the interior
@@ -64,6 +64,18 @@ struct StepArgs {
     void* B;                    // B' = a I + b A + c A^2
     float* partial;             // wg_norm partial sums of squares per tile
 };
+
+// Index of the class holding tile t: the last entry with tile_base <= t
+// (binary search over the launch table; the search is uniform per wave).
+__host__ __device__ inline int find_class(const MatEntry* mats, int n, int t) {
+    int lo = 0, hi = n - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (mats[mid].tile_base <= t) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo;
+}
 
 // ---- tile geometry ---------------------------------------------------------
 // On the step path every tile is stored oriented (r = min(h, w) rows,

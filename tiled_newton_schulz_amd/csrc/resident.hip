@@ -157,10 +157,7 @@ __global__ __launch_bounds__(64) void resident_kernel(const ResidentArgs args) {
 
     // ---- which tile: class by scalar scan of the launch table ----
     const int t = blockIdx.x;
-    int mi = 0;
-    for (int i = 1; i < args.nmats; ++i)
-        if (t >= args.mats[i].tile_base) mi = i;
-    const MatEntry& me = args.mats[mi];
+    const MatEntry& me = args.mats[find_class(args.mats, args.nmats, t)];
     const TileGeom tg = class_tile(me, args.T, t - me.tile_base);
     const int r0 = tg.r0, c0 = tg.c0, h = tg.h, w = tg.w;
 

@@ -57,9 +57,7 @@ struct TileRef {
 };
 
 __device__ __forceinline__ TileRef find_tile(const StepArgs& a, int t) {
-    int mi = 0;
-    for (int i = 1; i < a.nmats; ++i)
-        if (t >= a.mats[i].tile_base) mi = i;
+    const int mi = find_class(a.mats, a.nmats, t);
     const MatEntry& me = a.mats[mi];
     TileRef r;
     r.mi = mi;
