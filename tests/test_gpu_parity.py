@@ -312,3 +312,17 @@ def test_dense8192_cap(cuda, T):
         run(ref_mats, T, cap=1 << 40)
         for a, b in zip(mats, ref_mats):
             assert torch.equal(a, b)
+
+
+def test_tail_split_bit_exact(cuda):
+    """The partial last round of kernel-tile-128 tiles runs four waves per tile;
+    its arithmetic is the one-wave kernel's, so a batched call (3,072 tiles
+    one-wave + 64 four-wave) equals matrix-by-matrix calls bit for bit."""
+    w = WORKLOADS["layer_d2048"]
+    base = [t.cuda() for t in workloads.host_tensors(w)]
+    batched = [b.clone() for b in base]
+    run(batched, 128)
+    for b, m in zip(base, batched):
+        single = b.clone()
+        run([single], 128)
+        assert torch.equal(single, m)

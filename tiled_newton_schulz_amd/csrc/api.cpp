@@ -354,6 +354,23 @@ MatEntry entry_of(const MatSpec& s, const TileClass& c, int64_t tile_base, int64
     return e;
 }
 
+// One-wave kernel-tile-128 slots and CU count of the current device, queried
+// once per device.
+struct SlotInfo {
+    int slots, cus;
+};
+SlotInfo slot_info(bool muon) {
+    static SlotInfo cache[2][64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return SlotInfo{0, 0};
+    SlotInfo& c = cache[muon ? 1 : 0][dev];
+    if (c.cus == 0) {
+        c.slots = resident_slots(128, muon, false);
+        c.cus = device_cus();
+    }
+    return c;
+}
+
 himuon_status_t hip_fail(hipError_t e) {
     g_last_hip = (int32_t)e;
     return HIMUON_ERR_HIP;
@@ -382,8 +399,26 @@ himuon_status_t run(const std::vector<MatSpec>& specs, int32_t T, int32_t K, con
         a.eps = eps;
         a.mu = mu;
         a.eta = eta;
+        // Tiles beyond the last full round of one-wave tiles go to the
+        // four-waves-per-tile kernel (kernel tile 128), which finishes a
+        // partial round in about a third of a tile time.
+        int32_t split = a.total_tiles;
+        if (G.kernel_tile == 128 && !G.precise) {
+            const SlotInfo si = slot_info(muon);
+            if (si.slots > 0 && si.cus > 0) {
+                const int32_t rem = a.total_tiles % si.slots;
+                if (rem > 0 && rem <= 2 * si.cus) split = a.total_tiles - rem;
+            }
+        }
+        a.tile_begin = 0;
+        a.tile_end = split;
         hipError_t e = launch_resident(a, G.kernel_tile, muon, G.precise, s);
         if (e != hipSuccess) return hip_fail(e);
+        if (split < a.total_tiles) {
+            a.tile_begin = split;
+            a.tile_end = a.total_tiles;
+            if ((e = launch_resident_coop(a, muon, s)) != hipSuccess) return hip_fail(e);
+        }
     }
 
     for (const Chunk& c : plan.chunks) {

@@ -32,7 +32,9 @@ struct ResidentArgs {
     MatEntry mats[kGroup];
     float abc[3 * kMaxSteps];
     int32_t nmats;
-    int32_t total_tiles;
+    int32_t total_tiles;  // tiles of the launch table
+    int32_t tile_begin;   // this launch runs tiles [tile_begin, tile_end)
+    int32_t tile_end;
     int32_t T;           // grid tile size: tile (i, j) starts at (i T, j T)
     int32_t K;
     float eps;
@@ -108,6 +110,9 @@ __host__ __device__ inline TileGeom class_tile(const MatEntry& e, int32_t T, int
 
 // Host-side launchers (defined in the .hip files).
 hipError_t launch_resident(const ResidentArgs& a, int kernel_tile, bool muon, bool precise, hipStream_t s);
+hipError_t launch_resident_coop(const ResidentArgs& a, bool muon, hipStream_t s);
+int resident_slots(int kernel_tile, bool muon, bool precise);   // tiles the device holds at once (0 on error)
+int device_cus();
 hipError_t launch_step_norm(const StepArgs& a, hipStream_t s);
 hipError_t launch_step_gram(const StepArgs& a, hipStream_t s);
 hipError_t launch_step_poly(const StepArgs& a, hipStream_t s);

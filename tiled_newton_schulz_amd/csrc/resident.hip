@@ -23,6 +23,9 @@
 // AL(X) is read from LDS (X stored row-major, bf16) with ds_read_tr16_b64,
 // which gives the one transpose per step its 8-byte reads.
 //
+// The b A + c A^2 epilogue is written with an explicit fma so that every
+// kernel rounds it the same way.
+//
 // Precision (bf16 MFMA operands, fp32 accumulation):
 //  * kernel tiles 32 and 64 keep the tile in fp32 registers; X' = a X starts
 //    from fp32 and X is rounded to bf16 only as an MFMA operand.  Kernel tile
@@ -156,7 +159,7 @@ __global__ __launch_bounds__(64) void resident_kernel(const ResidentArgs args) {
     const int g = lane >> 5;
 
     // ---- which tile: class by scalar scan of the launch table ----
-    const int t = blockIdx.x;
+    const int t = args.tile_begin + blockIdx.x;
     const MatEntry& me = args.mats[find_class(args.mats, args.nmats, t)];
     const TileGeom tg = class_tile(me, args.T, t - me.tile_base);
     const int r0 = tg.r0, c0 = tg.c0, h = tg.h, w = tg.w;
@@ -187,7 +190,7 @@ __global__ __launch_bounds__(64) void resident_kernel(const ResidentArgs args) {
             }
             chunk[it] = v;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) { float x = bf2f(v[e]); ss += x * x; }
+            for (int e = 0; e < 8; ++e) { float x = bf2f(v[e]); ss = __builtin_fmaf(x, x, ss); }
         }
     }
     ss = wave_sum(ss);
@@ -398,11 +401,11 @@ __global__ __launch_bounds__(64) void resident_kernel(const ResidentArgs args) {
 #pragma unroll
                     for (int k = 0; k < 4; ++k) {
                         const int e = 8 * f + 2 * k;
-                        a1[e] = cb * lo_f(Abf[P1][Q1][f][k]) + cc * a1[e];
-                        a1[e + 1] = cb * hi_f(Abf[P1][Q1][f][k]) + cc * a1[e + 1];
+                        a1[e] = __builtin_fmaf(cc, a1[e], cb * lo_f(Abf[P1][Q1][f][k]));
+                        a1[e + 1] = __builtin_fmaf(cc, a1[e + 1], cb * hi_f(Abf[P1][Q1][f][k]));
                         if (two) {
-                            a2[e] = cb * lo_f(Abf[P2][Q2][f][k]) + cc * a2[e];
-                            a2[e + 1] = cb * hi_f(Abf[P2][Q2][f][k]) + cc * a2[e + 1];
+                            a2[e] = __builtin_fmaf(cc, a2[e], cb * lo_f(Abf[P2][Q2][f][k]));
+                            a2[e + 1] = __builtin_fmaf(cc, a2[e + 1], cb * hi_f(Abf[P2][Q2][f][k]));
                         }
                     }
                 Bbf[P1][Q1][0] = cvt8(a1, 0); Bbf[P1][Q1][1] = cvt8(a1, 8);
@@ -439,13 +442,13 @@ __global__ __launch_bounds__(64) void resident_kernel(const ResidentArgs args) {
                         const int e = 8 * f + 2 * k;
                         float A0 = lo_f(Abf[P][Q][f][k]), A1 = hi_f(Abf[P][Q][f][k]);
                         if constexpr (SPLIT_A) { A0 += lo_f(Alo[P][Q][f][k]); A1 += hi_f(Alo[P][Q][f][k]); }
-                        a1[e] = cb * A0 + cc * a1[e];
-                        a1[e + 1] = cb * A1 + cc * a1[e + 1];
+                        a1[e] = __builtin_fmaf(cc, a1[e], cb * A0);
+                        a1[e + 1] = __builtin_fmaf(cc, a1[e + 1], cb * A1);
                         if (Q != P) {
                             float C0 = lo_f(Abf[Q][P][f][k]), C1 = hi_f(Abf[Q][P][f][k]);
                             if constexpr (SPLIT_A) { C0 += lo_f(Alo[Q][P][f][k]); C1 += hi_f(Alo[Q][P][f][k]); }
-                            a2[e] = cb * C0 + cc * a2[e];
-                            a2[e + 1] = cb * C1 + cc * a2[e + 1];
+                            a2[e] = __builtin_fmaf(cc, a2[e], cb * C0);
+                            a2[e + 1] = __builtin_fmaf(cc, a2[e + 1], cb * C1);
                         }
                     }
                 Bbf[P][Q][0] = cvt8(a1, 0); Bbf[P][Q][1] = cvt8(a1, 8);
@@ -541,10 +544,248 @@ __global__ __launch_bounds__(64) void resident_kernel(const ResidentArgs args) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Cooperative variant for kernel tile 128: four waves share one tile, for the
+// last, partly filled round of tiles, which would otherwise leave most SIMDs
+// idle for a whole tile time.  X stays in LDS (bf16, row-major); wave w owns
+// column block w of A and of B' and row block w of X':
+//   A(I, w)     = sum_k RF(X(I,.)) . RF(X(w,.))          (operands from LDS)
+//   B'(P, w)    = a I + b A(P,w) + c sum_K AL(A(K,P)) . AL(A(K,w))
+//                 (AL(A(K,P)) of the other waves' columns read from LDS)
+//   X'^T(J, w)  = sum_K AL(X(K,J)) . AL(B'(K,w))         -> RL(X'(w, J))
+// The arithmetic per element is the same as the one-wave kernel's.
+// ---------------------------------------------------------------------------
+template <bool MUON>
+__global__ __launch_bounds__(256) void resident_coop_kernel(const ResidentArgs args) {
+    constexpr int TK = 128, NB = 4, LD = TK + 8, NK = TK / 16;
+    __shared__ __attribute__((aligned(16))) unsigned short sX[TK * LD];
+    __shared__ __attribute__((aligned(16))) u32x4 sA[NB * NB * 2 * 64];   // AL fragments, lane-major
+    __shared__ float red[4];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, w = tid >> 6;
+    const int l32 = lane & 31, g = lane >> 5;
+
+    const int t = args.tile_begin + blockIdx.x;
+    const MatEntry& me = args.mats[find_class(args.mats, args.nmats, t)];
+    const TileGeom tg = class_tile(me, args.T, t - me.tile_base);
+    const int h = tg.h, wd = tg.w;
+    unsigned short* mbase = reinterpret_cast<unsigned short*>(me.m) + (int64_t)tg.r0 * me.m_ld + tg.c0;
+    const bool mvec = vec_ok(me.m, me.m_ld, tg.c0);
+    using IO = TileIO<TK>;
+    constexpr int NCH = TK * IO::CPR / 256;   // 16-byte chunks per thread
+
+    // ---- load (Muon: M <- mu M + G, stored), sum of squares, normalise ----
+    u16x8 chunk[NCH];
+    float ss = 0.f;
+    {
+        const unsigned short* gbase = nullptr;
+        bool gvec = false;
+        if constexpr (MUON) {
+            gbase = reinterpret_cast<const unsigned short*>(me.g) + (int64_t)tg.r0 * me.g_ld + tg.c0;
+            gvec = vec_ok(me.g, me.g_ld, tg.c0);
+        }
+#pragma unroll
+        for (int it = 0; it < NCH; ++it) {
+            const int idx = it * 256 + tid;
+            const int r = idx / IO::CPR, col = (idx % IO::CPR) * 8;
+            u16x8 v = IO::load(mbase, me.m_ld, r, col, h, wd, mvec);
+            if constexpr (MUON) {
+                u16x8 gv = IO::load(gbase, me.g_ld, r, col, h, wd, gvec);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] = f2bf(args.mu * bf2f(v[e]) + bf2f(gv[e]));
+                IO::store(mbase, me.m_ld, r, col, h, wd, mvec, v);
+            }
+            chunk[it] = v;
+            *reinterpret_cast<u16x8*>(&sX[r * LD + col]) = v;
+        }
+    }
+    __syncthreads();
+    // The sum of squares is taken by wave 0 in exactly the one-wave kernel's
+    // order (lane l sums chunks l, l + 64, ...), so a tile's result does not
+    // depend on which kernel ran it.
+    if (w == 0) {
+#pragma unroll
+        for (int it = 0; it < IO::NCH; ++it) {
+            const int idx = it * 64 + lane;
+            const int r = idx / IO::CPR, col = (idx % IO::CPR) * 8;
+            const u16x8 v = *reinterpret_cast<const u16x8*>(&sX[r * LD + col]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) { float x = bf2f(v[e]); ss = __builtin_fmaf(x, x, ss); }
+        }
+        ss = wave_sum(ss);
+        if (lane == 0) red[0] = ss;
+    }
+    __syncthreads();
+    ss = red[0];
+    const float scale = 1.0f / (sqrtf(ss) + args.eps);
+#pragma unroll
+    for (int it = 0; it < NCH; ++it) {
+        const int idx = it * 256 + tid;
+        const int r = idx / IO::CPR, col = (idx % IO::CPR) * 8;
+        u16x8 v;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = f2bf(bf2f(chunk[it][e]) * scale);
+        *reinterpret_cast<u16x8*>(&sX[r * LD + col]) = v;
+    }
+    __syncthreads();
+
+    auto rl_off = [&](int I, int J, int m) { return (I * 32 + l32) * LD + J * 32 + 8 * m + 4 * g; };
+    auto tr_frag = [&](int K, int J, int f) {
+        const int G = lane >> 4, i16 = lane & 15;
+        const int col = J * 32 + 16 * (G & 1) + 4 * (i16 & 3);
+        const int rowb = K * 32 + 16 * f + 4 * g + (i16 >> 2);
+        bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(&sX[rowb * LD + col]));
+        bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(&sX[(rowb + 8) * LD + col]));
+        return __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    auto afrag = [&](int K, int P, int f) -> u32x4& { return sA[((K * NB + P) * 2 + f) * 64 + lane]; };
+
+    for (int step = 0; step < args.K; ++step) {
+        const float ca = args.abc[3 * step], cb = args.abc[3 * step + 1], cc = args.abc[3 * step + 2];
+        u32x4 Aown[NB][2];   // AL(A(I, w))
+        u32x4 Bown[NB][2];   // AL(B'(P, w))
+        {
+            u32x4 RF[NB][NK];
+#pragma unroll
+            for (int I = 0; I < NB; ++I)
+#pragma unroll
+                for (int kc = 0; kc < NK; ++kc)
+                    RF[I][kc] = *reinterpret_cast<const u32x4*>(&sX[(I * 32 + l32) * LD + kc * 16 + g * 8]);
+            u32x4 RFw[NK];
+#pragma unroll
+            for (int kc = 0; kc < NK; ++kc)
+                RFw[kc] = *reinterpret_cast<const u32x4*>(&sX[(w * 32 + l32) * LD + kc * 16 + g * 8]);
+            f32x16 acc[NB];
+#pragma unroll
+            for (int I = 0; I < NB; ++I) acc[I] = f32x16{};
+#pragma unroll
+            for (int kc = 0; kc < NK; ++kc)
+#pragma unroll
+                for (int I = 0; I < NB; ++I) acc[I] = mfma32w(RF[I][kc], RFw[kc], acc[I]);
+#pragma unroll
+            for (int I = 0; I < NB; ++I) {
+                Aown[I][0] = cvt8(acc[I], 0);
+                Aown[I][1] = cvt8(acc[I], 8);
+                afrag(I, w, 0) = Aown[I][0];
+                afrag(I, w, 1) = Aown[I][1];
+            }
+        }
+        __syncthreads();
+        {
+            f32x16 acc[NB];
+#pragma unroll
+            for (int P = 0; P < NB; ++P) acc[P] = f32x16{};
+#pragma unroll
+            for (int K = 0; K < NB; ++K)
+#pragma unroll
+                for (int f = 0; f < 2; ++f)
+#pragma unroll
+                    for (int P = 0; P < NB; ++P) acc[P] = mfma32w(afrag(K, P, f), Aown[K][f], acc[P]);
+#pragma unroll
+            for (int P = 0; P < NB; ++P) {
+                if (P == w) {
+#pragma unroll
+                    for (int q = 0; q < 16; ++q)
+                        if ((q >> 2) * 8 + g * 4 + (q & 3) == l32) acc[P][q] += ca / cc;
+                }
+#pragma unroll
+                for (int f = 0; f < 2; ++f)
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const int e = 8 * f + 2 * k;
+                        acc[P][e] = __builtin_fmaf(cc, acc[P][e], cb * lo_f(Aown[P][f][k]));
+                        acc[P][e + 1] = __builtin_fmaf(cc, acc[P][e + 1], cb * hi_f(Aown[P][f][k]));
+                    }
+                Bown[P][0] = cvt8(acc[P], 0);
+                Bown[P][1] = cvt8(acc[P], 8);
+            }
+        }
+        {
+            f32x16 acc[NB];
+#pragma unroll
+            for (int J = 0; J < NB; ++J) acc[J] = f32x16{};
+#pragma unroll
+            for (int K = 0; K < NB; ++K)
+#pragma unroll
+                for (int f = 0; f < 2; ++f)
+#pragma unroll
+                    for (int J = 0; J < NB; ++J) acc[J] = mfma32w(tr_frag(K, J, f), Bown[K][f], acc[J]);
+            __syncthreads();   // every wave has read X (and A) for this step
+#pragma unroll
+            for (int J = 0; J < NB; ++J)
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    u32x2 v = {pack2(acc[J][4 * m], acc[J][4 * m + 1]), pack2(acc[J][4 * m + 2], acc[J][4 * m + 3])};
+                    *reinterpret_cast<u32x2*>(&sX[rl_off(w, J, m)]) = v;
+                }
+            __syncthreads();
+        }
+    }
+
+    // ---- write back in place (Muon: W <- W - eta X) ----
+    unsigned short* obase = mbase;
+    int64_t old = me.m_ld;
+    bool ovec = mvec;
+    if constexpr (MUON) {
+        obase = reinterpret_cast<unsigned short*>(me.w) + (int64_t)tg.r0 * me.w_ld + tg.c0;
+        old = me.w_ld;
+        ovec = vec_ok(me.w, me.w_ld, tg.c0);
+    }
+#pragma unroll
+    for (int it = 0; it < NCH; ++it) {
+        const int idx = it * 256 + tid;
+        const int r = idx / IO::CPR, col = (idx % IO::CPR) * 8;
+        u16x8 v = *reinterpret_cast<const u16x8*>(&sX[r * LD + col]);
+        if constexpr (MUON) {
+            u16x8 wv = IO::load(obase, old, r, col, h, wd, ovec);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = f2bf(bf2f(wv[e]) - args.eta * bf2f(v[e]));
+        }
+        IO::store(obase, old, r, col, h, wd, ovec, v);
+    }
+}
+
 template <int TK, bool MUON, bool PRECISE>
 static hipError_t launch_tk(const ResidentArgs& a, hipStream_t s) {
-    if (a.total_tiles <= 0) return hipSuccess;
-    hipLaunchKernelGGL((resident_kernel<TK, MUON, PRECISE>), dim3(a.total_tiles), dim3(64), 0, s, a);
+    const int n = a.tile_end - a.tile_begin;
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL((resident_kernel<TK, MUON, PRECISE>), dim3(n), dim3(64), 0, s, a);
+    return hipGetLastError();
+}
+
+template <int TK, bool MUON, bool PRECISE>
+static int slots_tk() {
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, resident_kernel<TK, MUON, PRECISE>, 64, 0) != hipSuccess)
+        return 0;
+    return per_cu * device_cus();
+}
+
+int device_cus() {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    return cus;
+}
+
+int resident_slots(int kernel_tile, bool muon, bool precise) {
+    if (precise) return 0;
+    switch (kernel_tile) {
+        case 32: return muon ? slots_tk<32, true, false>() : slots_tk<32, false, false>();
+        case 64: return muon ? slots_tk<64, true, false>() : slots_tk<64, false, false>();
+        case 128: return muon ? slots_tk<128, true, false>() : slots_tk<128, false, false>();
+        default: return 0;
+    }
+}
+
+hipError_t launch_resident_coop(const ResidentArgs& a, bool muon, hipStream_t s) {
+    const int n = a.tile_end - a.tile_begin;
+    if (n <= 0) return hipSuccess;
+    if (muon)
+        hipLaunchKernelGGL((resident_coop_kernel<true>), dim3(n), dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL((resident_coop_kernel<false>), dim3(n), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
