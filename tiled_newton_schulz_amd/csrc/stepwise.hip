@@ -106,24 +106,82 @@ __global__ __launch_bounds__(256) void step_norm_kernel(const StepArgs a) {
     ET* mbase = reinterpret_cast<ET*>(me.m) + (int64_t)g.r0 * me.m_ld + g.c0;
     const int sbw = (g.w + 63) / 64, sbh = (g.h + 63) / 64;
     const int tid = threadIdx.x;
+    // each thread moves runs of 8 consecutive elements: row tid/8 (+32), columns 8 (tid%8) ..
+    const int rr = tid >> 3, cc8 = (tid & 7) * 8;
+
+    // 8 elements of row i starting at column j of a matrix, masked to w columns
+    auto load8 = [&](const ET* base, int64_t ld, int i, int j, int w, float (&v)[8]) {
+        const ET* p = base + (int64_t)i * ld + j;
+        if (j + 8 <= w && ((reinterpret_cast<uintptr_t>(p) & (8 * sizeof(ET) - 1)) == 0)) {
+            if constexpr (IO == 0) {
+                const u16x8 u = *reinterpret_cast<const u16x8*>(p);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] = bf2f(u[e]);
+            } else {
+                const float4 u0 = *reinterpret_cast<const float4*>(p);
+                const float4 u1 = *reinterpret_cast<const float4*>(p + 4);
+                v[0] = u0.x; v[1] = u0.y; v[2] = u0.z; v[3] = u0.w;
+                v[4] = u1.x; v[5] = u1.y; v[6] = u1.z; v[7] = u1.w;
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = (j + e < w) ? E::ld(p + e) : 0.f;
+        }
+    };
+    auto store8 = [&](ET* base, int64_t ld, int i, int j, int w, const float (&v)[8]) {
+        ET* p = base + (int64_t)i * ld + j;
+        if (j + 8 <= w && ((reinterpret_cast<uintptr_t>(p) & (8 * sizeof(ET) - 1)) == 0)) {
+            if constexpr (IO == 0) {
+                u16x8 u;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) u[e] = f2bf(v[e]);
+                *reinterpret_cast<u16x8*>(p) = u;
+            } else {
+                *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+                *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (j + e < w) p[e] = E::cv(v[e]);
+        }
+    };
+    // 8 workspace elements (rows padded to a multiple of 8, so always whole)
+    auto wstore8 = [&](WT* p, const float (&v)[8]) {
+        if constexpr (WK == 0) {
+            u16x8 u;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) u[e] = f2bf(v[e]);
+            *reinterpret_cast<u16x8*>(p) = u;
+        } else {
+            *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+            *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+        }
+    };
 
     if (PASS == 0) {
         const ET* gbase = a.muon ? reinterpret_cast<const ET*>(me.g) + (int64_t)g.r0 * me.g_ld + g.c0 : nullptr;
         float ss = 0.f;
         for (int sb = k; sb < sbw * sbh; sb += a.wg_norm) {
             const int i0 = (sb / sbw) * 64, j0 = (sb % sbw) * 64;
-            for (int e = tid; e < 64 * 64; e += 256) {
-                const int i = i0 + e / 64, j = j0 + e % 64;
-                if (i < g.h && j < g.w) {
-                    ET* p = mbase + (int64_t)i * me.m_ld + j;
-                    float x = E::ld(p);
-                    if (a.muon) {
-                        ET nv = E::cv(a.mu * x + E::ld(gbase + (int64_t)i * me.g_ld + j));
-                        *p = nv;
-                        x = E::ld(&nv);
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const int i = i0 + rr + 32 * half, j = j0 + cc8;
+                if (i >= g.h || j >= g.w) continue;
+                float v[8];
+                load8(mbase, me.m_ld, i, j, g.w, v);
+                if (a.muon) {
+                    float gv[8];
+                    load8(gbase, me.g_ld, i, j, g.w, gv);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const ET nv = E::cv(a.mu * v[e] + gv[e]);
+                        v[e] = E::ld(&nv);
                     }
-                    ss += x * x;
+                    store8(mbase, me.m_ld, i, j, g.w, v);
                 }
+#pragma unroll
+                for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(v[e], v[e], ss);
             }
         }
         ss = block_sum(ss, red);
@@ -136,42 +194,75 @@ __global__ __launch_bounds__(256) void step_norm_kernel(const StepArgs a) {
     const float scale = 1.0f / (sqrtf(tot) + a.eps);
     WT* xo = reinterpret_cast<WT*>(a.Xc) + g.xoff;
     const int64_t xld = round8(g.s);
+    ET* wbase = a.muon ? reinterpret_cast<ET*>(me.w) + (int64_t)g.r0 * me.w_ld + g.c0 : nullptr;
     for (int sb = k; sb < sbw * sbh; sb += a.wg_norm) {
         const int i0 = (sb / sbw) * 64, j0 = (sb % sbw) * 64;
-        if (a.K == 0) {
-            // output = normalised tile, in place (Muon: W -= eta * it)
-            ET* wbase = a.muon ? reinterpret_cast<ET*>(me.w) + (int64_t)g.r0 * me.w_ld + g.c0 : nullptr;
-            for (int e = tid; e < 64 * 64; e += 256) {
-                const int i = i0 + e / 64, j = j0 + e % 64;
-                if (i < g.h && j < g.w) {
-                    const float y = E::ld(mbase + (int64_t)i * me.m_ld + j) * scale;
+        if (a.K == 0 || !g.tr) {
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const int i = i0 + rr + 32 * half, j = j0 + cc8;
+                if (i >= g.h || j >= g.w) continue;
+                float v[8];
+                load8(mbase, me.m_ld, i, j, g.w, v);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] *= scale;
+                if (a.K == 0) {
+                    // output = normalised tile, in place (Muon: W -= eta * it)
                     if (a.muon) {
-                        ET* wp = wbase + (int64_t)i * me.w_ld + j;
-                        *wp = E::cv(E::ld(wp) - a.eta * y);
+                        float wv[8];
+                        load8(wbase, me.w_ld, i, j, g.w, wv);
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            const ET r = E::cv(v[e]);
+                            wv[e] = wv[e] - a.eta * E::ld(&r);
+                        }
+                        store8(wbase, me.w_ld, i, j, g.w, wv);
                     } else {
-                        mbase[(int64_t)i * me.m_ld + j] = E::cv(y);
+                        store8(mbase, me.m_ld, i, j, g.w, v);
+                    }
+                } else {
+                    // row i of the tile; its padding columns stay unwritten (masked by readers)
+                    if (j + 8 <= g.w) {
+                        wstore8(xo + (int64_t)i * xld + j, v);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            if (j + e < g.w) xo[(int64_t)i * xld + j + e] = EW::cv(v[e]);
                     }
                 }
             }
-            continue;
-        }
-        if (!g.tr) {
-            for (int e = tid; e < 64 * 64; e += 256) {
-                const int i = i0 + e / 64, j = j0 + e % 64;
-                if (i < g.h && j < g.w) xo[(int64_t)i * xld + j] = EW::cv(E::ld(mbase + (int64_t)i * me.m_ld + j) * scale);
-            }
         } else {
-            // tall tile: stored transposed, through LDS so both sides coalesce
-            for (int e = tid; e < 64 * 64; e += 256) {
-                const int i = e / 64, j = e % 64;
-                float v = 0.f;
-                if (i0 + i < g.h && j0 + j < g.w) v = E::ld(mbase + (int64_t)(i0 + i) * me.m_ld + j0 + j) * scale;
-                tileT[i][j] = v;
+            // tall tile: stored transposed, through LDS so both sides move whole runs
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const int i = rr + 32 * half;
+                float v[8];
+                if (i0 + i < g.h && j0 + cc8 < g.w) {
+                    load8(mbase, me.m_ld, i0 + i, j0 + cc8, g.w, v);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) v[e] = 0.f;
+                }
+#pragma unroll
+                for (int e = 0; e < 8; ++e) tileT[i][cc8 + e] = v[e] * scale;
             }
             __syncthreads();
-            for (int e = tid; e < 64 * 64; e += 256) {
-                const int j = e / 64, i = e % 64;   // oriented row j (original column), column i
-                if (i0 + i < g.h && j0 + j < g.w) xo[(int64_t)(j0 + j) * xld + i0 + i] = EW::cv(tileT[i][j]);
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const int j = rr + 32 * half;        // oriented row (original column j0 + j)
+                if (j0 + j < g.w && i0 + cc8 < g.h) {
+                    float v[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) v[e] = tileT[cc8 + e][j];
+                    WT* p = xo + (int64_t)(j0 + j) * xld + i0 + cc8;
+                    if (i0 + cc8 + 8 <= g.h) {
+                        wstore8(p, v);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            if (i0 + cc8 + e < g.h) p[e] = EW::cv(v[e]);
+                    }
+                }
             }
             __syncthreads();
         }
@@ -184,9 +275,9 @@ __global__ __launch_bounds__(256) void step_norm_kernel(const StepArgs a) {
 // MODE 0 gram:  C = X X^T          (r x r, contraction over s), lower blocks
 // MODE 1 poly:  C = A A, B' = a I + b A + c C                   lower blocks
 // MODE 2 apply: C = B' X           (r x s, contraction over r)
-// bf16: v_mfma_f32_32x32x16_bf16, k chunk 32; fp32: v_mfma_f32_32x32x2f32,
-// k chunk 16.  Row operands are read from LDS along k; the X operand of apply
-// (k along rows of X) uses ds_read_tr16_b64 for bf16.
+// bf16: v_mfma_f32_32x32x16_bf16, k chunk 64; fp32: v_mfma_f32_32x32x2f32,
+// k chunk 32; two LDS stages.  Row operands are read from LDS along k; the X
+// operand of apply (k along rows of X) uses ds_read_tr16_b64 for bf16.
 // ---------------------------------------------------------------------------
 // Final result element (i, j) of a tile, in place in the matrix dtype (Muon:
 // W <- W - eta * result, with the result rounded to the dtype first, as the
@@ -206,14 +297,21 @@ __device__ __forceinline__ void store_out(const StepArgs& a, const MatEntry& me,
     }
 }
 
+// k chunk of the step GEMMs (tuning knobs; multiples of 32)
+#ifndef HIMUON_STEP_BK_BF16
+#define HIMUON_STEP_BK_BF16 64
+#endif
+#ifndef HIMUON_STEP_BK_FP32
+#define HIMUON_STEP_BK_FP32 32
+#endif
 template <int DT> struct GemmCfg;
 template <> struct GemmCfg<0> {
-    static constexpr int BK = 32, EPC = 8;         // k chunk, elements per 16-byte chunk
+    static constexpr int BK = HIMUON_STEP_BK_BF16, EPC = 8;         // k chunk, elements per 16-byte chunk
     static constexpr int LDP = BK + 8;             // row-panel stride (elements)
     static constexpr int LDN = 128 + 16;           // X-panel stride for apply
 };
 template <> struct GemmCfg<1> {
-    static constexpr int BK = 16, EPC = 4;
+    static constexpr int BK = HIMUON_STEP_BK_FP32, EPC = 4;
     static constexpr int LDP = BK + 1;
     static constexpr int LDN = 128 + 4;
 };
@@ -225,8 +323,10 @@ __global__ __launch_bounds__(256) void step_gemm_kernel(const StepArgs a) {
     using C = GemmCfg<DT>;
     constexpr int BK = C::BK, EPC = C::EPC, LDP = C::LDP, LDN = C::LDN;
     constexpr bool NN = MODE == 2;
-    __shared__ __attribute__((aligned(16))) ET sP[128 * LDP];
-    __shared__ __attribute__((aligned(16))) ET sQ[NN ? BK * LDN : 128 * LDP];
+    // two stages of the row panel P and of the second operand Q
+    constexpr int PSZ = 128 * LDP, QSZ = NN ? BK * LDN : 128 * LDP;
+    __shared__ __attribute__((aligned(16))) ET sP2[2 * PSZ];
+    __shared__ __attribute__((aligned(16))) ET sQ2[2 * QSZ];
 
     // ---- workgroup -> (tile, block), blocks of one tile on one XCD ----
     const int nwg = a.grid_blocks;
@@ -277,11 +377,13 @@ __global__ __launch_bounds__(256) void step_gemm_kernel(const StepArgs a) {
     const int wm = wave >> 1, wn = wave & 1;
     const int l32 = lane & 31, gl = lane >> 5;
 
-    // global -> register staging: 2 chunks of 16 bytes per panel per thread
-    u32x4 rp[2], rq[2];
+    // global -> register staging: NCP chunks of 16 bytes per panel per thread
+    constexpr int NCP = 128 * BK / EPC / 256;
+    static_assert(NCP * 256 * EPC == 128 * BK, "panel chunks must cover the panel");
+    u32x4 rp[NCP], rq[NCP];
     auto load_panels = [&](int k0) {
 #pragma unroll
-        for (int p = 0; p < 2; ++p) {
+        for (int p = 0; p < NCP; ++p) {
             const int c = tid + 256 * p;
             {   // P: 128 rows x BK
                 const int row = c / (BK / EPC), kc = (c % (BK / EPC)) * EPC;
@@ -327,9 +429,11 @@ __global__ __launch_bounds__(256) void step_gemm_kernel(const StepArgs a) {
             }
         }
     };
-    auto store_panels = [&]() {
+    auto store_panels = [&](int stage) {
+        ET* sP = sP2 + stage * PSZ;
+        ET* sQ = sQ2 + stage * QSZ;
 #pragma unroll
-        for (int p = 0; p < 2; ++p) {
+        for (int p = 0; p < NCP; ++p) {
             const int c = tid + 256 * p;
             const int row = c / (BK / EPC), kc = (c % (BK / EPC)) * EPC;
             if (DT == 0) {
@@ -359,12 +463,9 @@ __global__ __launch_bounds__(256) void step_gemm_kernel(const StepArgs a) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
 
-    load_panels(0);
-    for (int k0 = 0; k0 < kdim; k0 += BK) {
-        __syncthreads();
-        store_panels();
-        __syncthreads();
-        if (k0 + BK < kdim) load_panels(k0 + BK);
+    auto compute = [&](int stage) {
+        const ET* sP = sP2 + stage * PSZ;
+        const ET* sQ = sQ2 + stage * QSZ;
         if constexpr (DT == 0) {
 #pragma unroll
             for (int kk = 0; kk < BK / 16; ++kk) {
@@ -410,10 +511,46 @@ __global__ __launch_bounds__(256) void step_gemm_kernel(const StepArgs a) {
                         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[i], bv[j], acc[i][j], 0, 0, 0);
             }
         }
+    };
+
+    // pipeline: the next k chunk is loaded to registers while the current one
+    // is multiplied from LDS; one barrier per chunk
+    const int nk = (kdim + BK - 1) / BK;
+    load_panels(0);
+    store_panels(0);
+    __syncthreads();
+    // poly: the epilogue needs A over this output block, which (A being
+    // symmetric) is the k range [n0 + wn 64 + j 32, +32) of the row panel, so it
+    // is taken from LDS while that chunk is resident
+    float aval[2][2][16];
+    for (int kt = 0; kt < nk; ++kt) {
+        if (kt + 1 < nk) load_panels((kt + 1) * BK);
+        compute(kt & 1);
+        if constexpr (MODE == 1) {
+            const ET* sP = sP2 + (kt & 1) * PSZ;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int c0 = n0 + wn * 64 + j * 32;
+                if (kt == c0 / BK) {
+                    const int cl = c0 - kt * BK + l32;
+#pragma unroll
+                    for (int i = 0; i < 2; ++i)
+#pragma unroll
+                        for (int q = 0; q < 16; ++q) {
+                            const int rl = wm * 64 + i * 32 + (q >> 2) * 8 + gl * 4 + (q & 3);
+                            aval[i][j][q] = E::ld(&sP[rl * LDP + cl]);
+                        }
+                }
+            }
+        }
+        if (kt + 1 < nk) store_panels((kt + 1) & 1);
+        __syncthreads();
     }
 
     // ---- epilogue: lane l, register q of block (i,j) holds
-    //      C[m0 + wm*64 + i*32 + rho(l,q)][n0 + wn*64 + j*32 + l%32] ----
+    //      C[m0 + wm*64 + i*32 + rho(l,q)][n0 + wn*64 + j*32 + l%32]; the four
+    //      registers 4m..4m+3 are four consecutive rows, so a transposed
+    //      (mirrored) store writes them as one run ----
     const float ca = a.abc[3 * a.step], cb = a.abc[3 * a.step + 1], cc = a.abc[3 * a.step + 2];
     const bool last = (MODE == 2) && (a.step == a.K - 1);
     const MatEntry& me = a.mats[tref.mi];
@@ -422,38 +559,65 @@ __global__ __launch_bounds__(256) void step_gemm_kernel(const StepArgs a) {
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
-            for (int q = 0; q < 16; ++q) {
-                const int row = m0 + wm * 64 + i * 32 + (q >> 2) * 8 + gl * 4 + (q & 3);
+            for (int m = 0; m < 4; ++m) {
+                const int row0 = m0 + wm * 64 + i * 32 + m * 8 + gl * 4;   // rows row0 .. row0+3
                 const int col = n0 + wn * 64 + j * 32 + l32;
-                float v = acc[i][j][q];
-                if (MODE == 0) {
-                    if (row < g.r && col < g.r) {
-                        ET* Ao = reinterpret_cast<ET*>(a.A) + g.aoff;
-                        const int64_t ld = round8(g.r);
-                        const ET e = E::cv(v);
-                        Ao[(int64_t)row * ld + col] = e;
-                        if (bm != bn) Ao[(int64_t)col * ld + row] = e;
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * m + e];
+                if (MODE == 0 || MODE == 1) {
+                    if (col >= g.r) continue;
+                    const int64_t ld = round8(g.r);
+                    ET* Out = reinterpret_cast<ET*>(MODE == 0 ? a.A : a.B) + g.aoff;
+                    if (MODE == 1) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            if (row0 + e < g.r) {
+                                float bv = __builtin_fmaf(cc, v[e], cb * aval[i][j][4 * m + e]);
+                                if (row0 + e == col) bv += ca;
+                                v[e] = bv;
+                            }
+                        }
                     }
-                } else if (MODE == 1) {
-                    if (row < g.r && col < g.r) {
-                        const ET* Ai = reinterpret_cast<const ET*>(a.A) + g.aoff;
-                        ET* Bo = reinterpret_cast<ET*>(a.B) + g.aoff;
-                        const int64_t ld = round8(g.r);
-                        float bv = cb * E::ld(Ai + (int64_t)row * ld + col) + cc * v;
-                        if (row == col) bv += ca;
-                        const ET e = E::cv(bv);
-                        Bo[(int64_t)row * ld + col] = e;
-                        if (bm != bn) Bo[(int64_t)col * ld + row] = e;
+                    ET o[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) o[e] = E::cv(v[e]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (row0 + e < g.r) Out[(int64_t)(row0 + e) * ld + col] = o[e];
+                    if (bm != bn) {
+                        // mirror: row col, columns row0 .. row0+3 (8-aligned rows, so whole runs)
+                        ET* mp = Out + (int64_t)col * ld + row0;
+                        if (row0 + 4 <= g.r) {
+                            if constexpr (DT == 0) {
+                                u32x2 pk = {(unsigned)__builtin_bit_cast(unsigned short, o[0]) |
+                                                ((unsigned)__builtin_bit_cast(unsigned short, o[1]) << 16),
+                                            (unsigned)__builtin_bit_cast(unsigned short, o[2]) |
+                                                ((unsigned)__builtin_bit_cast(unsigned short, o[3]) << 16)};
+                                *reinterpret_cast<u32x2*>(mp) = pk;
+                            } else {
+                                *reinterpret_cast<float4*>(mp) = make_float4(o[0], o[1], o[2], o[3]);
+                            }
+                        } else {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                if (row0 + e < g.r) mp[e] = o[e];
+                        }
                     }
                 } else {
-                    if (row < g.r && col < g.s) {
-                        if (!last) {
-                            ET* Xo = reinterpret_cast<ET*>(a.Xn) + g.xoff;
-                            Xo[(int64_t)row * round8(g.s) + col] = E::cv(v);
-                        } else {
-                            const int oi = g.tr ? col : row, oj = g.tr ? row : col;
-                            if (a.io_dtype == 0) store_out<0>(a, me, g, oi, oj, v);
-                            else store_out<1>(a, me, g, oi, oj, v);
+                    if (col >= g.s) continue;
+                    if (!last) {
+                        ET* Xo = reinterpret_cast<ET*>(a.Xn) + g.xoff;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (row0 + e < g.r) Xo[(int64_t)(row0 + e) * round8(g.s) + col] = E::cv(v[e]);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            if (row0 + e >= g.r) continue;
+                            const int oi = g.tr ? col : row0 + e, oj = g.tr ? row0 + e : col;
+                            if (a.io_dtype == 0) store_out<0>(a, me, g, oi, oj, v[e]);
+                            else store_out<1>(a, me, g, oi, oj, v[e]);
                         }
                     }
                 }
