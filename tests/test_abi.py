@@ -70,9 +70,9 @@ def test_validation_errors_before_any_launch():
     assert call_ns([H.himuon_matrix_t((1 << 20) + 1, 64, 64, 64)]) == 3   # misaligned bf16
     assert call_ns([H.himuon_matrix_t((1 << 20) + 2, 64, 64, 64)], dt=H.FP32, T=256) == 3
     # the step path needs a workspace
-    assert call_ns([sd(512, 512)], T=256) == 5
-    assert call_ns([sd(512, 512)], T=256, ws=None, ws_bytes=1 << 20) == 5
-    assert call_ns([sd(512, 512)], T=256, ws=ctypes.c_void_p(1 << 30), ws_bytes=1000) == 5
+    assert call_ns([sd(1024, 1024)], T=512) == 5
+    assert call_ns([sd(1024, 1024)], T=512, ws=None, ws_bytes=1 << 20) == 5
+    assert call_ns([sd(1024, 1024)], T=512, ws=ctypes.c_void_p(1 << 30), ws_bytes=1000) == 5
 
 
 def test_overlap_detection():
@@ -142,25 +142,39 @@ def test_plan_cross_layer_groups():
     assert info["resident_launches"] == math.ceil(168 / 256)
 
 
-def test_plan_moe_ragged_and_chunking():
+def moe_descs():
     descs, p = [], 1 << 32
     for _ in range(64):
         for h, w in ((4096, 1408), (1408, 4096)):
             descs.append(sd(h, w, ptr=p))
             p += h * w * 2 + 4096
-    full, mn = H.himuon_workspace_size(descs, 256, H.BF16)
-    assert full > mn > 0
-    info = H.himuon_plan(descs, 256, 5, H.BF16, full)
-    # 10,240 full tiles and 2,048 ragged 256x128 / 128x256 edge tiles
+    return descs
+
+
+def test_plan_moe_ragged_on_chip():
+    descs = moe_descs()
+    info = H.himuon_plan(descs, 256, 5, H.BF16)
+    # 10,240 full tiles and 2,048 ragged 256x128 / 128x256 edge tiles, all on
+    # chip (kernel tile 256), two tile classes per matrix, 256 classes a launch
     assert info["tiles"] == 64 * 2 * 16 * 6
-    # two tile classes per matrix (interior and one edge), 256 classes per group
+    assert info["kernel_tile"] == 256 and info["chunks"] == 0 and info["workspace_full"] == 0
+    assert info["resident_launches"] == math.ceil(2 * len(descs) / 256)
+
+
+def test_plan_moe_chunking():
+    descs = moe_descs()
+    full, mn = H.himuon_workspace_size(descs, 512, H.BF16)
+    assert full > mn > 0
+    info = H.himuon_plan(descs, 512, 5, H.BF16, full)
+    # at T = 512 every tile takes the step path: 512x512 and 512x384 / 384x512
+    assert info["tiles"] == 64 * 2 * 8 * 3 and info["resident_launches"] == 0
     assert info["chunks"] == math.ceil(2 * len(descs) / 256)
     # a small cap forces many chunks, each within the cap
     cap = 64 << 20
-    info2 = H.himuon_plan(descs, 256, 5, H.BF16, cap)
+    info2 = H.himuon_plan(descs, 512, 5, H.BF16, cap)
     assert info2["chunks"] > info["chunks"] and info2["workspace_full"] <= cap
     with pytest.raises(H.HimuonError) as e:
-        H.himuon_plan(descs, 256, 5, H.BF16, mn - 1)
+        H.himuon_plan(descs, 512, 5, H.BF16, mn - 1)
     assert e.value.code == 5
 
 
@@ -171,8 +185,8 @@ def test_plan_dense_cap():
         info = H.himuon_plan(d, T, 5, H.BF16, 4 << 30)
         assert info["workspace_full"] <= 4 << 30
         assert info["tiles"] == 2 * (8192 // T) * (28672 // T)
-        if T == 128:
-            assert info["resident_launches"] == 1 and info["chunks"] == 0
+        if T <= 256:
+            assert info["resident_launches"] == 1 and info["chunks"] == 0 and info["kernel_tile"] == T
         else:
             assert info["chunks"] >= math.ceil(full / (4 << 30))
 
@@ -191,7 +205,7 @@ def test_plan_full_matrix_and_fp32():
 
 def route(th, tw):
     mn, mx = min(th, tw), max(th, tw)
-    if mx <= 128 and mn >= 32:
+    if mx <= 256 and mn >= 32:
         return "chip"
     if mx <= 64:
         return "chip-precise"

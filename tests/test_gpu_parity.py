@@ -101,8 +101,20 @@ def test_bf16_on_chip_shapes(cuda, T):
         assert err <= TOL["bf16"], (h, w, T, err)
 
 
+@pytest.mark.parametrize("T", [256, 4096])
+def test_bf16_kernel_tile_256_shapes(cuda, T):
+    """Tiles whose larger side is 129..256 (zero padded to 256 x 256 on chip),
+    including thin, ragged and transposed shapes."""
+    rng = np.random.default_rng([25, T])
+    for (h, w) in [(256, 256), (256, 32), (32, 256), (200, 150), (130, 256), (256, 129), (171, 40), (97, 230)]:
+        x = workloads.round_to(rng.standard_normal((h, w)), "bf16")
+        err, _ = full_check(x, T, "bf16")
+        say(f"bf16 {h}x{w} T={T}: {err:.3e}")
+        assert err <= TOL["bf16"], (h, w, T, err)
+
+
 @pytest.mark.parametrize("T", [160, 256, 512, 4096])
-def test_bf16_step_path_shapes(cuda, T):
+def test_bf16_large_tile_shapes(cuda, T):
     rng = np.random.default_rng([12, T])
     for (h, w) in [(300, 299), (129, 600), (600, 130), (513, 257), (700, 520)]:
         x = workloads.round_to(rng.standard_normal((h, w)), "bf16")
@@ -129,6 +141,31 @@ def test_step_counts_and_mixed_coefficients(cuda, dt, T, K):
     err, _ = full_check(x, T, dt, K=K, abc=MIXED[:K] if K else [])
     say(f"{dt} K={K} T={T}: {err:.3e}")
     assert err <= TOL[dt]
+
+
+# steps with c = 0 (the cubic iteration) mixed with quintic ones
+CUBIC_MIX = [(1.5, -0.5, 0.0), (3.4445, -4.7750, 2.0315), (1.5, -0.5, 0.0), (2.0, -1.5, 0.5), (1.5, -0.5, 0.0)]
+
+
+@pytest.mark.parametrize("dt,T", [("bf16", 32), ("bf16", 64), ("bf16", 128), ("bf16", 256), ("bf16", 512),
+                                  ("fp32", 64)])
+def test_steps_without_quintic_term(cuda, dt, T):
+    rng = np.random.default_rng([26, T])
+    x = workloads.round_to(rng.standard_normal((2 * T + 17, T + 9)), dt)
+    err, _ = full_check(x, T, dt, K=5, abc=CUBIC_MIX)
+    say(f"{dt} c=0 steps T={T}: {err:.3e}")
+    assert err <= TOL[dt]
+
+
+def test_steps_without_quintic_term_one_wave_kernel(cuda):
+    """Enough 128-tiles that most run in the one-wave kernel (a small call runs
+    in the four-wave kernel only)."""
+    rng = np.random.default_rng(27)
+    x = workloads.round_to(rng.standard_normal((128 * 4, 128 * 400)), "bf16").cuda()
+    sampled = grab([x], 128, 40, rng)
+    run([x], 128, K=5, abc=CUBIC_MIX)
+    worst = check_sampled(sampled, [x], 128, CUBIC_MIX, 5, TOL["bf16"])
+    say(f"  max err {worst:.3e}")
 
 
 def test_zero_and_tiny_tiles(cuda):
@@ -194,15 +231,17 @@ def test_column_blocks_of_fused_tensor(cuda):
         assert torch.equal(p, s_)
 
 
+@pytest.mark.parametrize("T", [256, 512])
 @pytest.mark.parametrize("cap_tiles", [1, 3, 7])
-def test_chunking_bit_exact(cuda, cap_tiles):
+def test_chunking_bit_exact(cuda, T, cap_tiles):
     rng = np.random.default_rng([18, cap_tiles])
-    xs = [workloads.round_to(rng.standard_normal(s), "bf16").cuda() for s in [(600, 520), (257, 513)]]
-    full, mn = H.himuon_workspace_size(xs, 256, H.BF16)
+    xs = [workloads.round_to(rng.standard_normal(s), "bf16").cuda() for s in [(600, 520), (257, 513), (1100, 1030)]]
+    full, mn = H.himuon_workspace_size(xs, T, H.BF16)
+    assert mn > 0
     a = [x.clone() for x in xs]
-    run(a, 256)
+    run(a, T)
     b = [x.clone() for x in xs]
-    run(b, 256, cap=mn * cap_tiles)
+    run(b, T, cap=mn * cap_tiles)
     for u, v in zip(a, b):
         assert torch.equal(u, v)
 

@@ -113,9 +113,9 @@ himuon_status_t check_abc(int32_t K, const float* abc) {
 // Each matrix is cut into up to four tile classes (interior T x T tiles, the
 // right-edge column, the bottom-edge row and the corner); all tiles of a class
 // share one shape, and each class is routed by that shape:
-//   bf16, both sides 32..128          -> on-chip kernel (kernel tile 32/64/128)
+//   bf16, both sides 32..256          -> on-chip kernel (kernel tile 32/64/128/256)
 //   bf16, a side < 32, both <= 64     -> on-chip kernel, hi/lo split precision
-//   bf16, both sides >= 32, one > 128 -> step path, bf16 workspace
+//   bf16, both sides >= 32, one > 256 -> step path, bf16 workspace
 //   bf16, a side < 32, one > 64       -> step path, fp32 workspace
 //   fp32                              -> step path, fp32 workspace
 struct TileClass {
@@ -129,14 +129,14 @@ enum class Route { OnChip, OnChipPrecise, StepBf16, StepFp32 };
 Route route_of(himuon_dtype_t dt, int32_t th, int32_t tw) {
     const int32_t mn = std::min(th, tw), mx = std::max(th, tw);
     if (dt == HIMUON_FP32) return Route::StepFp32;
-    if (mx <= 128 && mn >= 32) return Route::OnChip;
+    if (mx <= 256 && mn >= 32) return Route::OnChip;
     if (mx <= 64) return Route::OnChipPrecise;
     if (mn >= 32) return Route::StepBf16;
     return Route::StepFp32;
 }
 int kernel_tile_for(int32_t th, int32_t tw) {
     const int32_t e = std::max(th, tw);
-    return e <= 32 ? 32 : e <= 64 ? 64 : 128;
+    return e <= 32 ? 32 : e <= 64 ? 64 : e <= 128 ? 128 : 256;
 }
 int64_t tiles_of(int64_t rows, int64_t cols, int32_t T) {
     return ((rows + T - 1) / T) * ((cols + T - 1) / T);
@@ -198,7 +198,7 @@ himuon_status_t build_plan(const std::vector<MatSpec>& specs, int32_t T, int32_t
 
     // on-chip launches, keyed by (kernel tile, precision)
     for (int precise = 0; precise < 2; ++precise)
-        for (int kt : {32, 64, 128}) {
+        for (int kt : {32, 64, 128, 256}) {
             Group cur;
             cur.kernel_tile = kt;
             cur.precise = precise != 0;

@@ -37,101 +37,9 @@
 //    Gram matrix dominates): X, A and B all carried as bf16 hi/lo pairs, three
 //    products per contraction (the lo x lo term dropped).
 
-#include "common.h"
+#include "device_util.h"
 
 namespace himuon {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
-typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
-
-#define LDS_AS __attribute__((address_space(3)))
-
-namespace {
-
-__device__ __forceinline__ float bf2f(unsigned short u) { return __uint_as_float(((unsigned)u) << 16); }
-__device__ __forceinline__ unsigned short f2bf(float f) {
-    __bf16 b = (__bf16)f;
-    return __builtin_bit_cast(unsigned short, b);
-}
-// Two floats -> one word of two bf16 (round to nearest even), low half first.
-__device__ __forceinline__ unsigned pack2(float a, float b) {
-    bf16x2 v = {(__bf16)a, (__bf16)b};
-    return __builtin_bit_cast(unsigned, v);
-}
-__device__ __forceinline__ float lo_f(unsigned u) { return __uint_as_float(u << 16); }
-__device__ __forceinline__ float hi_f(unsigned u) { return __uint_as_float(u & 0xffff0000u); }
-
-// Registers off..off+7 of an accumulator block as one bf16 MFMA operand.
-__device__ __forceinline__ u32x4 cvt8(const f32x16& v, int off) {
-    u32x4 r;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) r[k] = pack2(v[off + 2 * k], v[off + 2 * k + 1]);
-    return r;
-}
-// The bf16 rounding error of those registers, itself rounded to bf16.
-__device__ __forceinline__ u32x4 cvt8_lo(const f32x16& v, int off, u32x4 hi) {
-    u32x4 r;
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-        r[k] = pack2(v[off + 2 * k] - lo_f(hi[k]), v[off + 2 * k + 1] - hi_f(hi[k]));
-    return r;
-}
-__device__ __forceinline__ f32x16 mfma32w(u32x4 a, u32x4 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
-                                                   c, 0, 0, 0);
-}
-
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
-}
-
-// Global <-> LDS tile movement in 16-byte chunks, masked to the h x w tile.
-template <int TK>
-struct TileIO {
-    static constexpr int CPR = TK / 8;            // chunks per row
-    static constexpr int NCH = TK * CPR / 64;     // chunks per lane
-
-    __device__ static u16x8 load(const unsigned short* base, int64_t ld, int r, int col, int h, int w, bool vec) {
-        u16x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (r < h) {
-            const unsigned short* p = base + (int64_t)r * ld + col;
-            if (vec && col + 8 <= w) {
-                v = *reinterpret_cast<const u16x8*>(p);
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    if (col + e < w) v[e] = p[e];
-            }
-        }
-        return v;
-    }
-    __device__ static void store(unsigned short* base, int64_t ld, int r, int col, int h, int w, bool vec, u16x8 v) {
-        if (r < h) {
-            unsigned short* p = base + (int64_t)r * ld + col;
-            if (vec && col + 8 <= w) {
-                *reinterpret_cast<u16x8*>(p) = v;
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    if (col + e < w) p[e] = v[e];
-            }
-        }
-    }
-};
-
-__device__ __forceinline__ bool vec_ok(const void* base, int64_t ld, int c0) {
-    return ((reinterpret_cast<uintptr_t>(base) & 15) == 0) && ((ld & 7) == 0) && ((c0 & 7) == 0);
-}
-
-}  // namespace
 
 template <int TK, bool MUON, bool PRECISE>
 __global__ __launch_bounds__(64) void resident_kernel(const ResidentArgs args) {
@@ -365,7 +273,8 @@ __global__ __launch_bounds__(64) void resident_kernel(const ResidentArgs args) {
         // B = b A + c A^2 (A symmetric: AL(A(K,P)) is the row operand of A(P,K))
         if constexpr (SYM) {
             // lower blocks (P >= Q), two chains at a time; the kernel tile 128
-            // path folds a X into the product: B' = a I + B
+            // path folds a X into the product: B' = a I + B (a added after
+            // the fma, so that c = 0 is handled too)
             constexpr int NL = NB * (NB + 1) / 2;
 #pragma unroll
             for (int p = 0; p < NL; p += 2) {
@@ -391,12 +300,6 @@ __global__ __launch_bounds__(64) void resident_kernel(const ResidentArgs args) {
                         if (two) a2 = mfma32w(Abf[K][P2][f], Abf[K][Q2][f], a2);
                     }
 #pragma unroll
-                for (int q = 0; q < 16; ++q) {
-                    const bool diag = (q >> 2) * 8 + g * 4 + (q & 3) == l32;
-                    if (P1 == Q1 && diag) a1[q] += ca / cc;
-                    if (two && P2 == Q2 && diag) a2[q] += ca / cc;
-                }
-#pragma unroll
                 for (int f = 0; f < 2; ++f)
 #pragma unroll
                     for (int k = 0; k < 4; ++k) {
@@ -408,6 +311,12 @@ __global__ __launch_bounds__(64) void resident_kernel(const ResidentArgs args) {
                             a2[e + 1] = __builtin_fmaf(cc, a2[e + 1], cb * hi_f(Abf[P2][Q2][f][k]));
                         }
                     }
+#pragma unroll
+                for (int q = 0; q < 16; ++q) {
+                    const bool diag = (q >> 2) * 8 + g * 4 + (q & 3) == l32;
+                    if (P1 == Q1 && diag) a1[q] += ca;
+                    if (two && P2 == Q2 && diag) a2[q] += ca;
+                }
                 Bbf[P1][Q1][0] = cvt8(a1, 0); Bbf[P1][Q1][1] = cvt8(a1, 8);
                 if (two) { Bbf[P2][Q2][0] = cvt8(a2, 0); Bbf[P2][Q2][1] = cvt8(a2, 8); }
                 if (P1 != Q1) transpose_al(0, Bbf[P1][Q1], Bbf[Q1][P1]);
@@ -684,11 +593,6 @@ __global__ __launch_bounds__(256) void resident_coop_kernel(const ResidentArgs a
                     for (int P = 0; P < NB; ++P) acc[P] = mfma32w(afrag(K, P, f), Aown[K][f], acc[P]);
 #pragma unroll
             for (int P = 0; P < NB; ++P) {
-                if (P == w) {
-#pragma unroll
-                    for (int q = 0; q < 16; ++q)
-                        if ((q >> 2) * 8 + g * 4 + (q & 3) == l32) acc[P][q] += ca / cc;
-                }
 #pragma unroll
                 for (int f = 0; f < 2; ++f)
 #pragma unroll
@@ -697,6 +601,11 @@ __global__ __launch_bounds__(256) void resident_coop_kernel(const ResidentArgs a
                         acc[P][e] = __builtin_fmaf(cc, acc[P][e], cb * lo_f(Aown[P][f][k]));
                         acc[P][e + 1] = __builtin_fmaf(cc, acc[P][e + 1], cb * hi_f(Aown[P][f][k]));
                     }
+                if (P == w) {
+#pragma unroll
+                    for (int q = 0; q < 16; ++q)
+                        if ((q >> 2) * 8 + g * 4 + (q & 3) == l32) acc[P][q] += ca;
+                }
                 Bown[P][0] = cvt8(acc[P], 0);
                 Bown[P][1] = cvt8(acc[P], 8);
             }
@@ -801,6 +710,7 @@ hipError_t launch_resident(const ResidentArgs& a, int kernel_tile, bool muon, bo
         case 32: return muon ? launch_tk<32, true, false>(a, s) : launch_tk<32, false, false>(a, s);
         case 64: return muon ? launch_tk<64, true, false>(a, s) : launch_tk<64, false, false>(a, s);
         case 128: return muon ? launch_tk<128, true, false>(a, s) : launch_tk<128, false, false>(a, s);
+        case 256: return launch_resident256(a, muon, s);
         default: return hipErrorInvalidValue;
     }
 }

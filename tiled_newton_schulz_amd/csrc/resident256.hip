@@ -1,0 +1,313 @@
+// On-chip tiled Newton-Schulz for bf16 tiles whose larger side is 129..256,
+// on gfx950.
+//
+// One workgroup of eight waves owns one tile (zero padded to 256 x 256) for
+// all K steps; a CU holds one tile.  The map is the per-tile Newton-Schulz
+// iteration of the HiMuon abstract, written as in the Gram Newton-Schulz page
+// (Algorithm 1): A = X X^T, B = b A + c A^2, X <- a X + B X.  Padding is exact:
+// the padded Gram matrix is block diagonal, so padded rows and columns stay 0.
+//
+// The LDS (160 KB) holds one 256 x 256 bf16 matrix at a time (132 KB with
+// row padding), in turn X, A and B' = a I + b A + c A^2:
+//   1. A = X X^T: the 36 lower 32x32 blocks, four or five per wave, from
+//      16-byte row fragments of X.  Each wave also copies its column block of
+//      X (32 columns) into registers, as the MFMA operand of step 3.
+//   2. A is written over X: each lower block as it is, and transposed as the
+//      upper block, so the stored A is exactly symmetric.
+//   3. A^2 = A A^T (A symmetric), same blocks and reads as 1; the epilogue
+//      forms B' from the same rounded A, and B' is written over A.
+//   4. X'^T(w, I) = sum_K X(K, w)^T B'(K, I): a operand = the wave's column
+//      block of X (registers), b operand = row fragments of B' (B' symmetric,
+//      so column I of B'(K, I) is row I of B'(I, K)).  The result lands in the
+//      row layout of X'(I, w) and is written with 8-byte stores over B'.
+// Waves w and w + 4 share a SIMD; the block lists give each SIMD nine of the
+// 36 lower blocks.
+//
+// Register layouts as in the kernel-tile-128 kernel: AL (accumulator layout)
+// lane l, register q holds M[rho(l,q)][l % 32], rho = (q/4)*8 + (l/32)*4 + q%4;
+// RL = AL of the transpose.
+
+#include "device_util.h"
+
+namespace himuon {
+
+namespace {
+
+constexpr int kT = 256, kLD = kT + 8, kNB = 8;
+
+// Lower 32x32 blocks (i, j), i >= j, of a symmetric 256 x 256 product, per wave.
+constexpr int kBlkN[8] = {4, 4, 4, 4, 5, 5, 5, 5};
+constexpr int kBlkI[8][5] = {{2, 2, 3, 3, 0}, {4, 4, 5, 5, 0}, {6, 6, 7, 7, 0}, {4, 4, 5, 5, 0},
+                             {6, 6, 7, 7, 0}, {6, 6, 7, 7, 1}, {1, 2, 3, 3, 4}, {5, 5, 6, 7, 7}};
+constexpr int kBlkJ[8][5] = {{0, 1, 0, 1, 0}, {0, 1, 0, 1, 0}, {0, 1, 0, 1, 0}, {2, 3, 2, 3, 0},
+                             {2, 3, 2, 3, 0}, {4, 5, 4, 5, 1}, {0, 2, 2, 3, 4}, {4, 5, 6, 6, 7}};
+
+constexpr bool uses_row(int w, int r) {
+    for (int b = 0; b < kBlkN[w]; ++b)
+        if (kBlkI[w][b] == r || kBlkJ[w][b] == r) return true;
+    return false;
+}
+
+// LDS pointers with the lane-dependent part of each access pattern folded in,
+// so that every access below is one of these plus a constant.
+struct LdsLanes {
+    const unsigned short* rf;   // row fragments:   (l%32) row, 8 (l/32) column
+    const unsigned short* cf;   // column fragments (transposing reads)
+    unsigned short* rl;         // row-layout runs:  (l%32) row, 4 (l/32) column
+    unsigned short* al;         // accumulator layout: 4 (l/32) row, (l%32) column
+};
+
+// 16-byte row fragment: row R*32 + l%32, columns k0 + 8 (l/32) .. +7.
+__device__ __forceinline__ u32x4 row_frag(const LdsLanes& L, int R, int k0) {
+    return *reinterpret_cast<const u32x4*>(&L.rf[R * 32 * kLD + k0]);
+}
+
+// Column fragment in natural k order: lane l gets rows k0 + 8 (l/32) .. +7 of
+// column c0 + l%32 (two transposing 8-byte reads).
+__device__ __forceinline__ u32x4 col_frag(const LdsLanes& L, int k0, int c0) {
+    bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(&L.cf[k0 * kLD + c0]));
+    bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(&L.cf[(k0 + 4) * kLD + c0]));
+    return __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Lower blocks of M M^T (M the LDS matrix) for wave W, accumulated in AL.
+template <int W>
+__device__ __forceinline__ void gram_lower(const LdsLanes& L, f32x16 (&acc)[5]) {
+#pragma unroll
+    for (int b = 0; b < 5; ++b) acc[b] = f32x16{};
+#pragma unroll
+    for (int kc = 0; kc < kT / 16; ++kc) {
+        u32x4 rf[kNB];
+#pragma unroll
+        for (int r = 0; r < kNB; ++r)
+            if (uses_row(W, r)) rf[r] = row_frag(L, r, kc * 16);
+#pragma unroll
+        for (int b = 0; b < kBlkN[W]; ++b) acc[b] = mfma32w(rf[kBlkI[W][b]], rf[kBlkJ[W][b]], acc[b]);
+    }
+}
+
+// Writes the wave's lower blocks (bf16 AL in p) into the LDS matrix as a full
+// symmetric matrix: block (j, i) from the row layout (8-byte stores), block
+// (i, j) for i != j from AL (2-byte stores).
+template <int W>
+__device__ __forceinline__ void store_sym(const LdsLanes& L, const u32x4 (&p)[5][2]) {
+#pragma unroll
+    for (int b = 0; b < kBlkN[W]; ++b) {
+        const int i = kBlkI[W][b], j = kBlkJ[W][b];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            u32x2 v = {p[b][m >> 1][2 * (m & 1)], p[b][m >> 1][2 * (m & 1) + 1]};
+            *reinterpret_cast<u32x2*>(&L.rl[j * 32 * kLD + i * 32 + 8 * m]) = v;
+        }
+        if (i != j) {
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const unsigned word = p[b][q >> 3][(q & 7) >> 1];
+                const unsigned short v = (q & 1) ? (unsigned short)(word >> 16) : (unsigned short)(word & 0xffffu);
+                L.al[(i * 32 + (q >> 2) * 8 + (q & 3)) * kLD + j * 32] = v;
+            }
+        }
+    }
+}
+
+// B' = c A^2 + b A (+ a on the diagonal), in place of the rounded A in p.
+template <int W>
+__device__ __forceinline__ void combine(f32x16 (&acc)[5], u32x4 (&p)[5][2], float ca, float cb, float cc,
+                                        int l32, int g) {
+#pragma unroll
+    for (int b = 0; b < kBlkN[W]; ++b) {
+#pragma unroll
+        for (int f = 0; f < 2; ++f)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int e = 8 * f + 2 * k;
+                acc[b][e] = __builtin_fmaf(cc, acc[b][e], cb * lo_f(p[b][f][k]));
+                acc[b][e + 1] = __builtin_fmaf(cc, acc[b][e + 1], cb * hi_f(p[b][f][k]));
+            }
+        if (kBlkI[W][b] == kBlkJ[W][b]) {
+#pragma unroll
+            for (int q = 0; q < 16; ++q)
+                if ((q >> 2) * 8 + g * 4 + (q & 3) == l32) acc[b][q] += ca;
+        }
+        p[b][0] = cvt8(acc[b], 0);
+        p[b][1] = cvt8(acc[b], 8);
+    }
+}
+
+// Runs F<w>(args...) for the wave index w (uniform, in a scalar register).
+#define HIMUON_PER_WAVE(w, F, ...)           \
+    switch (w) {                             \
+        case 0: F<0>(__VA_ARGS__); break;    \
+        case 1: F<1>(__VA_ARGS__); break;    \
+        case 2: F<2>(__VA_ARGS__); break;    \
+        case 3: F<3>(__VA_ARGS__); break;    \
+        case 4: F<4>(__VA_ARGS__); break;    \
+        case 5: F<5>(__VA_ARGS__); break;    \
+        case 6: F<6>(__VA_ARGS__); break;    \
+        default: F<7>(__VA_ARGS__); break;   \
+    }
+
+}  // namespace
+
+template <bool MUON>
+__global__ __launch_bounds__(512) void resident256_kernel(const ResidentArgs args) {
+    __shared__ __attribute__((aligned(16))) unsigned short sX[kT * kLD];
+    __shared__ float red[8];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, g = lane >> 5;
+
+    const int t = args.tile_begin + blockIdx.x;
+    const MatEntry& me = args.mats[find_class(args.mats, args.nmats, t)];
+    const TileGeom tg = class_tile(me, args.T, t - me.tile_base);
+    const int h = tg.h, wd = tg.w;
+    unsigned short* mbase = reinterpret_cast<unsigned short*>(me.m) + (int64_t)tg.r0 * me.m_ld + tg.c0;
+    const bool mvec = vec_ok(me.m, me.m_ld, tg.c0);
+    using IO = TileIO<kT>;
+    constexpr int NCH = kT * IO::CPR / 512;   // 16-byte chunks per thread
+
+    // ---- load (Muon: M <- mu M + G, stored) into LDS, sum of squares ----
+    {
+        float ss = 0.f;
+        const unsigned short* gbase = nullptr;
+        bool gvec = false;
+        if constexpr (MUON) {
+            gbase = reinterpret_cast<const unsigned short*>(me.g) + (int64_t)tg.r0 * me.g_ld + tg.c0;
+            gvec = vec_ok(me.g, me.g_ld, tg.c0);
+        }
+#pragma unroll 4
+        for (int it = 0; it < NCH; ++it) {
+            const int idx = it * 512 + tid;
+            const int r = idx / IO::CPR, col = (idx % IO::CPR) * 8;
+            u16x8 v = IO::load(mbase, me.m_ld, r, col, h, wd, mvec);
+            if constexpr (MUON) {
+                u16x8 gv = IO::load(gbase, me.g_ld, r, col, h, wd, gvec);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] = f2bf(args.mu * bf2f(v[e]) + bf2f(gv[e]));
+                IO::store(mbase, me.m_ld, r, col, h, wd, mvec, v);
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) { const float x = bf2f(v[e]); ss = __builtin_fmaf(x, x, ss); }
+            *reinterpret_cast<u16x8*>(&sX[r * kLD + col]) = v;
+        }
+        ss = wave_sum(ss);
+        if (lane == 0) red[w] = ss;
+        __syncthreads();
+        float tot = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) tot += red[i];
+        const float scale = 1.0f / (sqrtf(tot) + args.eps);
+        // each thread rescales the chunks it wrote
+#pragma unroll 4
+        for (int it = 0; it < NCH; ++it) {
+            const int idx = it * 512 + tid;
+            const int r = idx / IO::CPR, col = (idx % IO::CPR) * 8;
+            u16x8 v = *reinterpret_cast<const u16x8*>(&sX[r * kLD + col]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = f2bf(bf2f(v[e]) * scale);
+            *reinterpret_cast<u16x8*>(&sX[r * kLD + col]) = v;
+        }
+        __syncthreads();
+    }
+
+    for (int step = 0; step < args.K; ++step) {
+        const float ca = args.abc[3 * step], cb = args.abc[3 * step + 1], cc = args.abc[3 * step + 2];
+        // The lane parts of the LDS addresses pass through an empty asm every
+        // step; otherwise the compiler hoists the few hundred distinct LDS
+        // addresses of a step out of the loop and spills them.
+        int o_rf = l32 * kLD + g * 8;
+        int o_cf = (8 * g + ((lane & 15) >> 2)) * kLD + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+        int o_rl = l32 * kLD + 4 * g;
+        int o_al = 4 * g * kLD + l32;
+        asm volatile("" : "+v"(o_rf), "+v"(o_cf), "+v"(o_rl), "+v"(o_al));
+        const LdsLanes L{sX + o_rf, sX + o_cf, sX + o_rl, sX + o_al};
+        f32x16 acc[5];
+        u32x4 p[5][2];
+        // 1. lower blocks of A = X X^T; this wave's column block of X
+        HIMUON_PER_WAVE(w, gram_lower, L, acc);
+        u32x4 xf[kNB][2];
+#pragma unroll
+        for (int K = 0; K < kNB; ++K)
+#pragma unroll
+            for (int kc = 0; kc < 2; ++kc) xf[K][kc] = col_frag(L, K * 32 + kc * 16, w * 32);
+#pragma unroll
+        for (int b = 0; b < 5; ++b) {
+            p[b][0] = cvt8(acc[b], 0);
+            p[b][1] = cvt8(acc[b], 8);
+        }
+        __syncthreads();
+        // 2. A over X
+        HIMUON_PER_WAVE(w, store_sym, L, p);
+        __syncthreads();
+        // 3. A^2 = A A^T, B' = a I + b A + c A^2, B' over A
+        HIMUON_PER_WAVE(w, gram_lower, L, acc);
+        HIMUON_PER_WAVE(w, combine, acc, p, ca, cb, cc, l32, g);
+        __syncthreads();
+        HIMUON_PER_WAVE(w, store_sym, L, p);
+        __syncthreads();
+        // 4. X'^T(w, I) = sum_K X(K, w)^T B'(K, I), two row blocks I at a time
+        u32x4 xo[kNB][2];
+#pragma unroll
+        for (int I = 0; I < kNB; I += 2) {
+            f32x16 c0 = {}, c1 = {};
+#pragma unroll
+            for (int K = 0; K < kNB; ++K)
+#pragma unroll
+                for (int kc = 0; kc < 2; ++kc) {
+                    const int k0 = K * 32 + kc * 16;
+                    c0 = mfma32w(xf[K][kc], row_frag(L, I, k0), c0);
+                    c1 = mfma32w(xf[K][kc], row_frag(L, I + 1, k0), c1);
+                }
+            xo[I][0] = cvt8(c0, 0);
+            xo[I][1] = cvt8(c0, 8);
+            xo[I + 1][0] = cvt8(c1, 0);
+            xo[I + 1][1] = cvt8(c1, 8);
+        }
+        __syncthreads();
+        // X' over B': RL(X'(I, w)) -> row I*32 + l%32, columns w*32 + rho
+#pragma unroll
+        for (int I = 0; I < kNB; ++I)
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                u32x2 v = {xo[I][m >> 1][2 * (m & 1)], xo[I][m >> 1][2 * (m & 1) + 1]};
+                *reinterpret_cast<u32x2*>(&L.rl[I * 32 * kLD + w * 32 + 8 * m]) = v;
+            }
+        __syncthreads();
+    }
+
+    // ---- write back in place (Muon: W <- W - eta X) ----
+    unsigned short* obase = mbase;
+    int64_t old = me.m_ld;
+    bool ovec = mvec;
+    if constexpr (MUON) {
+        obase = reinterpret_cast<unsigned short*>(me.w) + (int64_t)tg.r0 * me.w_ld + tg.c0;
+        old = me.w_ld;
+        ovec = vec_ok(me.w, me.w_ld, tg.c0);
+    }
+#pragma unroll
+    for (int it = 0; it < NCH; ++it) {
+        const int idx = it * 512 + tid;
+        const int r = idx / IO::CPR, col = (idx % IO::CPR) * 8;
+        u16x8 v = *reinterpret_cast<const u16x8*>(&sX[r * kLD + col]);
+        if constexpr (MUON) {
+            u16x8 wv = IO::load(obase, old, r, col, h, wd, ovec);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = f2bf(bf2f(wv[e]) - args.eta * bf2f(v[e]));
+        }
+        IO::store(obase, old, r, col, h, wd, ovec, v);
+    }
+}
+
+hipError_t launch_resident256(const ResidentArgs& a, bool muon, hipStream_t s) {
+    const int n = a.tile_end - a.tile_begin;
+    if (n <= 0) return hipSuccess;
+    if (muon)
+        hipLaunchKernelGGL((resident256_kernel<true>), dim3(n), dim3(512), 0, s, a);
+    else
+        hipLaunchKernelGGL((resident256_kernel<false>), dim3(n), dim3(512), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace himuon

@@ -16,27 +16,11 @@
 // Workgroup -> (tile, block) ids are remapped so that the blocks of one tile
 // run on one XCD and share its L2.
 
-#include "common.h"
+#include "device_util.h"
 
 namespace himuon {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
-
-#define LDS_AS __attribute__((address_space(3)))
-
 namespace {
-
-__device__ __forceinline__ float bf2f(unsigned short u) { return __uint_as_float(((unsigned)u) << 16); }
-__device__ __forceinline__ unsigned short f2bf(float f) {
-    __bf16 b = (__bf16)f;
-    return __builtin_bit_cast(unsigned short, b);
-}
 
 // Element access for the two storage types.
 template <int DT> struct Elem;
