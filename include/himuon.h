@@ -81,12 +81,15 @@ typedef enum himuon_status {
 /* Summary of how a call would be carried out (host-side planning only). */
 typedef struct himuon_plan_info {
     int64_t tiles;            /* tiles over all matrices                              */
-    int64_t resident_launches;/* launches of the on-chip kernel (T <= 128, bf16)      */
+    int64_t resident_launches;/* launch groups of the on-chip kernels (tiles <= 256, bf16) */
     int64_t chunks;           /* chunks of the step-by-step path (0 if not used)      */
     int64_t launches;         /* total kernel launches one call enqueues              */
-    int64_t kernel_tile;      /* on-chip kernel size (32, 64 or 128), or 0            */
+    int64_t kernel_tile;      /* largest on-chip kernel size (32, 64, 128 or 256), or 0 */
     size_t  workspace_full;   /* bytes the step-by-step path needs for one chunk      */
     size_t  workspace_min;    /* bytes it needs for its largest single tile           */
+    int64_t tail_tiles;       /* 128-tiles of the partial last round, run four waves
+                                 per tile by a second launch on the current device
+                                 (0 when no device is visible)                        */
 } himuon_plan_info_t;
 
 /*

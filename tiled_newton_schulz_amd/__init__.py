@@ -33,7 +33,7 @@ class himuon_plan_info_t(ctypes.Structure):
     _fields_ = [("tiles", ctypes.c_int64), ("resident_launches", ctypes.c_int64),
                 ("chunks", ctypes.c_int64), ("launches", ctypes.c_int64),
                 ("kernel_tile", ctypes.c_int64), ("workspace_full", ctypes.c_size_t),
-                ("workspace_min", ctypes.c_size_t)]
+                ("workspace_min", ctypes.c_size_t), ("tail_tiles", ctypes.c_int64)]
 
 
 class HimuonError(RuntimeError):

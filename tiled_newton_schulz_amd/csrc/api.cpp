@@ -371,6 +371,18 @@ SlotInfo slot_info(bool muon) {
     return c;
 }
 
+// First tile of a group's partial last round, which goes to the four-waves-
+// per-tile kernel (kernel tile 128 only; a round is the number of tiles the
+// device holds at once).  Returns the group's tile count when there is none.
+int32_t tail_split(const Group& G, bool muon) {
+    const int32_t total = (int32_t)G.tiles;
+    if (G.kernel_tile != 128 || G.precise) return total;
+    const SlotInfo si = slot_info(muon);
+    if (si.slots <= 0 || si.cus <= 0) return total;
+    const int32_t rem = total % si.slots;
+    return (rem > 0 && rem <= 2 * si.cus) ? total - rem : total;
+}
+
 himuon_status_t hip_fail(hipError_t e) {
     g_last_hip = (int32_t)e;
     return HIMUON_ERR_HIP;
@@ -402,14 +414,7 @@ himuon_status_t run(const std::vector<MatSpec>& specs, int32_t T, int32_t K, con
         // Tiles beyond the last full round of one-wave tiles go to the
         // four-waves-per-tile kernel (kernel tile 128), which finishes a
         // partial round in about a third of a tile time.
-        int32_t split = a.total_tiles;
-        if (G.kernel_tile == 128 && !G.precise) {
-            const SlotInfo si = slot_info(muon);
-            if (si.slots > 0 && si.cus > 0) {
-                const int32_t rem = a.total_tiles % si.slots;
-                if (rem > 0 && rem <= 2 * si.cus) split = a.total_tiles - rem;
-            }
-        }
+        const int32_t split = tail_split(G, muon);
         a.tile_begin = 0;
         a.tile_end = split;
         hipError_t e = launch_resident(a, G.kernel_tile, muon, G.precise, s);
@@ -486,7 +491,14 @@ himuon_status_t himuon_plan(const himuon_matrix_t* m, int32_t n, int32_t T, int3
     info->resident_launches = (int64_t)plan.rgroups.size();
     info->chunks = (int64_t)plan.chunks.size();
     info->launches = plan.launches;
-    for (const auto& g : plan.rgroups) info->kernel_tile = std::max<int64_t>(info->kernel_tile, g.kernel_tile);
+    for (const auto& g : plan.rgroups) {
+        info->kernel_tile = std::max<int64_t>(info->kernel_tile, g.kernel_tile);
+        const int32_t split = tail_split(g, false);
+        if (split < g.tiles) {
+            info->tail_tiles += g.tiles - split;
+            info->launches += 1;
+        }
+    }
     info->workspace_full = plan.ws_full;
     info->workspace_min = plan.ws_min;
     return HIMUON_OK;
