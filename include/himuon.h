@@ -87,7 +87,7 @@ typedef struct himuon_plan_info {
     int64_t kernel_tile;      /* largest on-chip kernel size (32, 64, 128 or 256), or 0 */
     size_t  workspace_full;   /* bytes the step-by-step path needs for one chunk      */
     size_t  workspace_min;    /* bytes it needs for its largest single tile           */
-    int64_t tail_tiles;       /* 128-tiles of the partial last round, run four waves
+    int64_t tail_tiles;       /* 128-tiles of the partial last round, run eight waves
                                  per tile by a second launch on the current device
                                  (0 when no device is visible)                        */
 } himuon_plan_info_t;

@@ -159,7 +159,7 @@ def test_steps_without_quintic_term(cuda, dt, T):
 
 def test_steps_without_quintic_term_one_wave_kernel(cuda):
     """Enough 128-tiles that most run in the one-wave kernel (a small call runs
-    in the four-wave kernel only)."""
+    in the eight-wave kernel only)."""
     rng = np.random.default_rng(27)
     x = workloads.round_to(rng.standard_normal((128 * 4, 128 * 400)), "bf16").cuda()
     sampled = grab([x], 128, 40, rng)
@@ -354,9 +354,9 @@ def test_dense8192_cap(cuda, T):
 
 
 def test_tail_split_bit_exact(cuda):
-    """The partial last round of kernel-tile-128 tiles runs four waves per tile;
+    """The partial last round of kernel-tile-128 tiles runs eight waves per tile;
     its arithmetic is the one-wave kernel's, so a batched call (3,072 tiles
-    one-wave + 64 four-wave) equals matrix-by-matrix calls bit for bit."""
+    one-wave + 64 eight-wave) equals matrix-by-matrix calls bit for bit."""
     w = WORKLOADS["layer_d2048"]
     base = [t.cuda() for t in workloads.host_tensors(w)]
     batched = [b.clone() for b in base]

@@ -371,7 +371,7 @@ SlotInfo slot_info(bool muon) {
     return c;
 }
 
-// First tile of a group's partial last round, which goes to the four-waves-
+// First tile of a group's partial last round, which goes to the eight-waves-
 // per-tile kernel (kernel tile 128 only; a round is the number of tiles the
 // device holds at once).  Returns the group's tile count when there is none.
 int32_t tail_split(const Group& G, bool muon) {
@@ -412,7 +412,7 @@ himuon_status_t run(const std::vector<MatSpec>& specs, int32_t T, int32_t K, con
         a.mu = mu;
         a.eta = eta;
         // Tiles beyond the last full round of one-wave tiles go to the
-        // four-waves-per-tile kernel (kernel tile 128), which finishes a
+        // eight-waves-per-tile kernel (kernel tile 128), which finishes a
         // partial round in about a third of a tile time.
         const int32_t split = tail_split(G, muon);
         a.tile_begin = 0;

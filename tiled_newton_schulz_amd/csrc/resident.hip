@@ -454,39 +454,44 @@ __global__ __launch_bounds__(64) void resident_kernel(const ResidentArgs args) {
 }
 
 // ---------------------------------------------------------------------------
-// Cooperative variant for kernel tile 128: four waves share one tile, for the
-// last, partly filled round of tiles, which would otherwise leave most SIMDs
-// idle for a whole tile time.  X stays in LDS (bf16, row-major); wave w owns
-// column block w of A and of B' and row block w of X':
-//   A(I, w)     = sum_k RF(X(I,.)) . RF(X(w,.))          (operands from LDS)
-//   B'(P, w)    = a I + b A(P,w) + c sum_K AL(A(K,P)) . AL(A(K,w))
-//                 (AL(A(K,P)) of the other waves' columns read from LDS)
-//   X'^T(J, w)  = sum_K AL(X(K,J)) . AL(B'(K,w))         -> RL(X'(w, J))
-// The arithmetic per element is the same as the one-wave kernel's.
+// Cooperative variant for kernel tile 128: eight waves (two per SIMD) share
+// one tile, for the last, partly filled round of tiles, which would otherwise
+// leave most SIMDs idle for a whole tile time.  X stays in LDS (bf16,
+// row-major); wave w owns column block c = w % 4 and the pair 2h, 2h + 1 with
+// h = w / 4:
+//   A(I, c)      I in {2h, 2h+1}  = sum_k RF(X(I,.)) . RF(X(c,.))
+//   B'(P, c)     P in {2h, 2h+1}  = a I + b A(P,c) + c sum_K AL(A(K,P)) . AL(A(K,c))
+//   X'^T(J, c)   J in {2h, 2h+1}  = sum_K AL(X(K,J)) . AL(B'(K,c))   -> RL(X'(c, J))
+// The AL fragments of A, then of B', pass through one LDS area.  Every
+// product takes the same operands in the same k order as in the one-wave
+// kernel (an upper block there is the transpose of the lower one, which is the
+// same product with its operands exchanged), and the sum of squares is taken in
+// the one-wave order, so a tile's result does not depend on which kernel ran it.
 // ---------------------------------------------------------------------------
 template <bool MUON>
-__global__ __launch_bounds__(256) void resident_coop_kernel(const ResidentArgs args) {
+__global__ __launch_bounds__(512) void resident_coop_kernel(const ResidentArgs args) {
     constexpr int TK = 128, NB = 4, LD = TK + 8, NK = TK / 16;
     __shared__ __attribute__((aligned(16))) unsigned short sX[TK * LD];
-    __shared__ __attribute__((aligned(16))) u32x4 sA[NB * NB * 2 * 64];   // AL fragments, lane-major
-    __shared__ float red[4];
+    __shared__ __attribute__((aligned(16))) u32x4 sF[NB * NB * 2 * 64];   // AL fragments, lane-major
+    __shared__ float red[1];
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, w = tid >> 6;
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int c = w & 3, h = w >> 2;
     const int l32 = lane & 31, g = lane >> 5;
 
     const int t = args.tile_begin + blockIdx.x;
     const MatEntry& me = args.mats[find_class(args.mats, args.nmats, t)];
     const TileGeom tg = class_tile(me, args.T, t - me.tile_base);
-    const int h = tg.h, wd = tg.w;
+    const int hh = tg.h, wd = tg.w;
     unsigned short* mbase = reinterpret_cast<unsigned short*>(me.m) + (int64_t)tg.r0 * me.m_ld + tg.c0;
     const bool mvec = vec_ok(me.m, me.m_ld, tg.c0);
     using IO = TileIO<TK>;
-    constexpr int NCH = TK * IO::CPR / 256;   // 16-byte chunks per thread
+    constexpr int NCH = TK * IO::CPR / 512;   // 16-byte chunks per thread
 
     // ---- load (Muon: M <- mu M + G, stored), sum of squares, normalise ----
     u16x8 chunk[NCH];
-    float ss = 0.f;
     {
         const unsigned short* gbase = nullptr;
         bool gvec = false;
@@ -496,24 +501,23 @@ __global__ __launch_bounds__(256) void resident_coop_kernel(const ResidentArgs a
         }
 #pragma unroll
         for (int it = 0; it < NCH; ++it) {
-            const int idx = it * 256 + tid;
+            const int idx = it * 512 + tid;
             const int r = idx / IO::CPR, col = (idx % IO::CPR) * 8;
-            u16x8 v = IO::load(mbase, me.m_ld, r, col, h, wd, mvec);
+            u16x8 v = IO::load(mbase, me.m_ld, r, col, hh, wd, mvec);
             if constexpr (MUON) {
-                u16x8 gv = IO::load(gbase, me.g_ld, r, col, h, wd, gvec);
+                u16x8 gv = IO::load(gbase, me.g_ld, r, col, hh, wd, gvec);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) v[e] = f2bf(args.mu * bf2f(v[e]) + bf2f(gv[e]));
-                IO::store(mbase, me.m_ld, r, col, h, wd, mvec, v);
+                IO::store(mbase, me.m_ld, r, col, hh, wd, mvec, v);
             }
             chunk[it] = v;
             *reinterpret_cast<u16x8*>(&sX[r * LD + col]) = v;
         }
     }
     __syncthreads();
-    // The sum of squares is taken by wave 0 in exactly the one-wave kernel's
-    // order (lane l sums chunks l, l + 64, ...), so a tile's result does not
-    // depend on which kernel ran it.
+    // sum of squares in the one-wave kernel's order (lane l sums chunks l, l + 64, ...)
     if (w == 0) {
+        float ss = 0.f;
 #pragma unroll
         for (int it = 0; it < IO::NCH; ++it) {
             const int idx = it * 64 + lane;
@@ -526,11 +530,10 @@ __global__ __launch_bounds__(256) void resident_coop_kernel(const ResidentArgs a
         if (lane == 0) red[0] = ss;
     }
     __syncthreads();
-    ss = red[0];
-    const float scale = 1.0f / (sqrtf(ss) + args.eps);
+    const float scale = 1.0f / (sqrtf(red[0]) + args.eps);
 #pragma unroll
     for (int it = 0; it < NCH; ++it) {
-        const int idx = it * 256 + tid;
+        const int idx = it * 512 + tid;
         const int r = idx / IO::CPR, col = (idx % IO::CPR) * 8;
         u16x8 v;
 #pragma unroll
@@ -539,7 +542,7 @@ __global__ __launch_bounds__(256) void resident_coop_kernel(const ResidentArgs a
     }
     __syncthreads();
 
-    auto rl_off = [&](int I, int J, int m) { return (I * 32 + l32) * LD + J * 32 + 8 * m + 4 * g; };
+    auto frag = [&](int K, int P, int f) -> u32x4& { return sF[((K * NB + P) * 2 + f) * 64 + lane]; };
     auto tr_frag = [&](int K, int J, int f) {
         const int G = lane >> 4, i16 = lane & 15;
         const int col = J * 32 + 16 * (G & 1) + 4 * (i16 & 3);
@@ -548,85 +551,85 @@ __global__ __launch_bounds__(256) void resident_coop_kernel(const ResidentArgs a
         bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(&sX[(rowb + 8) * LD + col]));
         return __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     };
-    auto afrag = [&](int K, int P, int f) -> u32x4& { return sA[((K * NB + P) * 2 + f) * 64 + lane]; };
 
     for (int step = 0; step < args.K; ++step) {
         const float ca = args.abc[3 * step], cb = args.abc[3 * step + 1], cc = args.abc[3 * step + 2];
-        u32x4 Aown[NB][2];   // AL(A(I, w))
-        u32x4 Bown[NB][2];   // AL(B'(P, w))
+        u32x4 Aown[2][2];   // AL(A(2h + i, c))
+        u32x4 Bown[2][2];   // AL(B'(2h + i, c))
         {
-            u32x4 RF[NB][NK];
+            f32x16 acc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-            for (int I = 0; I < NB; ++I)
+            for (int kc = 0; kc < NK; ++kc) {
+                const u32x4 rc = *reinterpret_cast<const u32x4*>(&sX[(c * 32 + l32) * LD + kc * 16 + g * 8]);
 #pragma unroll
-                for (int kc = 0; kc < NK; ++kc)
-                    RF[I][kc] = *reinterpret_cast<const u32x4*>(&sX[(I * 32 + l32) * LD + kc * 16 + g * 8]);
-            u32x4 RFw[NK];
+                for (int i = 0; i < 2; ++i) {
+                    const u32x4 ri =
+                        *reinterpret_cast<const u32x4*>(&sX[((2 * h + i) * 32 + l32) * LD + kc * 16 + g * 8]);
+                    acc[i] = mfma32w(ri, rc, acc[i]);
+                }
+            }
 #pragma unroll
-            for (int kc = 0; kc < NK; ++kc)
-                RFw[kc] = *reinterpret_cast<const u32x4*>(&sX[(w * 32 + l32) * LD + kc * 16 + g * 8]);
-            f32x16 acc[NB];
-#pragma unroll
-            for (int I = 0; I < NB; ++I) acc[I] = f32x16{};
-#pragma unroll
-            for (int kc = 0; kc < NK; ++kc)
-#pragma unroll
-                for (int I = 0; I < NB; ++I) acc[I] = mfma32w(RF[I][kc], RFw[kc], acc[I]);
-#pragma unroll
-            for (int I = 0; I < NB; ++I) {
-                Aown[I][0] = cvt8(acc[I], 0);
-                Aown[I][1] = cvt8(acc[I], 8);
-                afrag(I, w, 0) = Aown[I][0];
-                afrag(I, w, 1) = Aown[I][1];
+            for (int i = 0; i < 2; ++i) {
+                Aown[i][0] = cvt8(acc[i], 0);
+                Aown[i][1] = cvt8(acc[i], 8);
+                frag(2 * h + i, c, 0) = Aown[i][0];
+                frag(2 * h + i, c, 1) = Aown[i][1];
             }
         }
         __syncthreads();
         {
-            f32x16 acc[NB];
-#pragma unroll
-            for (int P = 0; P < NB; ++P) acc[P] = f32x16{};
+            f32x16 acc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
             for (int K = 0; K < NB; ++K)
 #pragma unroll
-                for (int f = 0; f < 2; ++f)
+                for (int f = 0; f < 2; ++f) {
+                    const u32x4 akc = frag(K, c, f);
 #pragma unroll
-                    for (int P = 0; P < NB; ++P) acc[P] = mfma32w(afrag(K, P, f), Aown[K][f], acc[P]);
+                    for (int i = 0; i < 2; ++i) acc[i] = mfma32w(frag(K, 2 * h + i, f), akc, acc[i]);
+                }
 #pragma unroll
-            for (int P = 0; P < NB; ++P) {
+            for (int i = 0; i < 2; ++i) {
 #pragma unroll
                 for (int f = 0; f < 2; ++f)
 #pragma unroll
                     for (int k = 0; k < 4; ++k) {
                         const int e = 8 * f + 2 * k;
-                        acc[P][e] = __builtin_fmaf(cc, acc[P][e], cb * lo_f(Aown[P][f][k]));
-                        acc[P][e + 1] = __builtin_fmaf(cc, acc[P][e + 1], cb * hi_f(Aown[P][f][k]));
+                        acc[i][e] = __builtin_fmaf(cc, acc[i][e], cb * lo_f(Aown[i][f][k]));
+                        acc[i][e + 1] = __builtin_fmaf(cc, acc[i][e + 1], cb * hi_f(Aown[i][f][k]));
                     }
-                if (P == w) {
+                if (2 * h + i == c) {
 #pragma unroll
                     for (int q = 0; q < 16; ++q)
-                        if ((q >> 2) * 8 + g * 4 + (q & 3) == l32) acc[P][q] += ca;
+                        if ((q >> 2) * 8 + g * 4 + (q & 3) == l32) acc[i][q] += ca;
                 }
-                Bown[P][0] = cvt8(acc[P], 0);
-                Bown[P][1] = cvt8(acc[P], 8);
+                Bown[i][0] = cvt8(acc[i], 0);
+                Bown[i][1] = cvt8(acc[i], 8);
             }
         }
-        {
-            f32x16 acc[NB];
+        __syncthreads();   // every wave has read A
 #pragma unroll
-            for (int J = 0; J < NB; ++J) acc[J] = f32x16{};
+        for (int i = 0; i < 2; ++i) {
+            frag(2 * h + i, c, 0) = Bown[i][0];
+            frag(2 * h + i, c, 1) = Bown[i][1];
+        }
+        __syncthreads();
+        {
+            f32x16 acc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
             for (int K = 0; K < NB; ++K)
 #pragma unroll
-                for (int f = 0; f < 2; ++f)
+                for (int f = 0; f < 2; ++f) {
+                    const u32x4 bkc = frag(K, c, f);
 #pragma unroll
-                    for (int J = 0; J < NB; ++J) acc[J] = mfma32w(tr_frag(K, J, f), Bown[K][f], acc[J]);
-            __syncthreads();   // every wave has read X (and A) for this step
+                    for (int j = 0; j < 2; ++j) acc[j] = mfma32w(tr_frag(K, 2 * h + j, f), bkc, acc[j]);
+                }
+            __syncthreads();   // every wave has read X (and B') for this step
 #pragma unroll
-            for (int J = 0; J < NB; ++J)
+            for (int j = 0; j < 2; ++j)
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
-                    u32x2 v = {pack2(acc[J][4 * m], acc[J][4 * m + 1]), pack2(acc[J][4 * m + 2], acc[J][4 * m + 3])};
-                    *reinterpret_cast<u32x2*>(&sX[rl_off(w, J, m)]) = v;
+                    u32x2 v = {pack2(acc[j][4 * m], acc[j][4 * m + 1]), pack2(acc[j][4 * m + 2], acc[j][4 * m + 3])};
+                    *reinterpret_cast<u32x2*>(&sX[(c * 32 + l32) * LD + (2 * h + j) * 32 + 8 * m + 4 * g]) = v;
                 }
             __syncthreads();
         }
@@ -643,15 +646,15 @@ __global__ __launch_bounds__(256) void resident_coop_kernel(const ResidentArgs a
     }
 #pragma unroll
     for (int it = 0; it < NCH; ++it) {
-        const int idx = it * 256 + tid;
+        const int idx = it * 512 + tid;
         const int r = idx / IO::CPR, col = (idx % IO::CPR) * 8;
         u16x8 v = *reinterpret_cast<const u16x8*>(&sX[r * LD + col]);
         if constexpr (MUON) {
-            u16x8 wv = IO::load(obase, old, r, col, h, wd, ovec);
+            u16x8 wv = IO::load(obase, old, r, col, hh, wd, ovec);
 #pragma unroll
             for (int e = 0; e < 8; ++e) v[e] = f2bf(bf2f(wv[e]) - args.eta * bf2f(v[e]));
         }
-        IO::store(obase, old, r, col, h, wd, ovec, v);
+        IO::store(obase, old, r, col, hh, wd, ovec, v);
     }
 }
 
@@ -692,9 +695,9 @@ hipError_t launch_resident_coop(const ResidentArgs& a, bool muon, hipStream_t s)
     const int n = a.tile_end - a.tile_begin;
     if (n <= 0) return hipSuccess;
     if (muon)
-        hipLaunchKernelGGL((resident_coop_kernel<true>), dim3(n), dim3(256), 0, s, a);
+        hipLaunchKernelGGL((resident_coop_kernel<true>), dim3(n), dim3(512), 0, s, a);
     else
-        hipLaunchKernelGGL((resident_coop_kernel<false>), dim3(n), dim3(256), 0, s, a);
+        hipLaunchKernelGGL((resident_coop_kernel<false>), dim3(n), dim3(512), 0, s, a);
     return hipGetLastError();
 }
 
