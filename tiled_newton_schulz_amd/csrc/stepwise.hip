@@ -16,6 +16,8 @@
 // Workgroup -> (tile, block) ids are remapped so that the blocks of one tile
 // run on one XCD and share its L2.
 
+#include <algorithm>
+
 #include "device_util.h"
 
 namespace himuon {
@@ -205,14 +207,9 @@ __global__ __launch_bounds__(256) void step_norm_kernel(const StepArgs a) {
                         store8(mbase, me.m_ld, i, j, g.w, v);
                     }
                 } else {
-                    // row i of the tile; its padding columns stay unwritten (masked by readers)
-                    if (j + 8 <= g.w) {
-                        wstore8(xo + (int64_t)i * xld + j, v);
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 8; ++e)
-                            if (j + e < g.w) xo[(int64_t)i * xld + j + e] = EW::cv(v[e]);
-                    }
+                    // row i of the tile, 8 elements; past w they are zero, so
+                    // the row's padding up to round8(w) is written as zeros
+                    wstore8(xo + (int64_t)i * xld + j, v);
                 }
             }
         } else {
@@ -238,14 +235,8 @@ __global__ __launch_bounds__(256) void step_norm_kernel(const StepArgs a) {
                     float v[8];
 #pragma unroll
                     for (int e = 0; e < 8; ++e) v[e] = tileT[cc8 + e][j];
-                    WT* p = xo + (int64_t)(j0 + j) * xld + i0 + cc8;
-                    if (i0 + cc8 + 8 <= g.h) {
-                        wstore8(p, v);
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 8; ++e)
-                            if (i0 + cc8 + e < g.h) p[e] = EW::cv(v[e]);
-                    }
+                    // 8 elements; past h they are zero (padding up to round8(h))
+                    wstore8(xo + (int64_t)(j0 + j) * xld + i0 + cc8, v);
                 }
             }
             __syncthreads();
@@ -281,6 +272,9 @@ __device__ __forceinline__ void store_out(const StepArgs& a, const MatEntry& me,
     }
 }
 
+#ifndef HIMUON_STEP_ASYNC
+#define HIMUON_STEP_ASYNC 1
+#endif
 // k chunk of the step GEMMs (tuning knobs; multiples of 32)
 #ifndef HIMUON_STEP_BK_BF16
 #define HIMUON_STEP_BK_BF16 64
@@ -299,6 +293,95 @@ template <> struct GemmCfg<1> {
     static constexpr int LDP = BK + 1;
     static constexpr int LDN = 128 + 4;
 };
+
+// Epilogue of the step GEMMs: lane l, register q of block (i,j) holds
+// C[m0 + wm*64 + i*32 + rho(l,q)][n0 + wn*64 + j*32 + l%32]; the four registers
+// 4m..4m+3 are four consecutive rows, so a transposed (mirrored) store writes
+// them as one run.  aval (poly only) holds A over the same positions.
+template <int DT, int MODE>
+__device__ __forceinline__ void gemm_epilogue(const StepArgs& a, const TileRef& tref, int bm, int bn, int m0,
+                                              int n0, int wm, int wn, int l32, int gl, const f32x16 (&acc)[2][2],
+                                              const float (&aval)[2][2][16]) {
+    using E = Elem<DT>;
+    using ET = typename E::T;
+    const TileGeom& g = tref.g;
+    const float ca = a.abc[3 * a.step], cb = a.abc[3 * a.step + 1], cc = a.abc[3 * a.step + 2];
+    const bool last = (MODE == 2) && (a.step == a.K - 1);
+    const MatEntry& me = a.mats[tref.mi];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int row0 = m0 + wm * 64 + i * 32 + m * 8 + gl * 4;   // rows row0 .. row0+3
+                const int col = n0 + wn * 64 + j * 32 + l32;
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * m + e];
+                if (MODE == 0 || MODE == 1) {
+                    // columns up to the padded row length are written: past r
+                    // the product is exactly zero (zero operand rows), which
+                    // keeps the padding of A and B' zero for readers that do not
+                    // mask it
+                    const int64_t ld = round8(g.r);
+                    if (col >= ld) continue;
+                    ET* Out = reinterpret_cast<ET*>(MODE == 0 ? a.A : a.B) + g.aoff;
+                    if (MODE == 1) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            if (row0 + e < g.r) {
+                                float bv = __builtin_fmaf(cc, v[e], cb * aval[i][j][4 * m + e]);
+                                if (row0 + e == col && col < g.r) bv += ca;
+                                v[e] = bv;
+                            }
+                        }
+                    }
+                    ET o[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) o[e] = E::cv(v[e]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (row0 + e < g.r) Out[(int64_t)(row0 + e) * ld + col] = o[e];
+                    if (bm != bn && col < g.r) {
+                        // mirror: row col, columns row0 .. row0+3 (rows are
+                        // padded to 8 elements, so a run is whole or outside)
+                        ET* mp = Out + (int64_t)col * ld + row0;
+                        if (row0 + 4 <= ld) {
+                            if constexpr (DT == 0) {
+                                u32x2 pk = {(unsigned)__builtin_bit_cast(unsigned short, o[0]) |
+                                                ((unsigned)__builtin_bit_cast(unsigned short, o[1]) << 16),
+                                            (unsigned)__builtin_bit_cast(unsigned short, o[2]) |
+                                                ((unsigned)__builtin_bit_cast(unsigned short, o[3]) << 16)};
+                                *reinterpret_cast<u32x2*>(mp) = pk;
+                            } else {
+                                *reinterpret_cast<float4*>(mp) = make_float4(o[0], o[1], o[2], o[3]);
+                            }
+                        } else {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                if (row0 + e < g.r) mp[e] = o[e];
+                        }
+                    }
+                } else {
+                    if (col >= (last ? g.s : round8(g.s))) continue;
+                    if (!last) {
+                        ET* Xo = reinterpret_cast<ET*>(a.Xn) + g.xoff;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (row0 + e < g.r) Xo[(int64_t)(row0 + e) * round8(g.s) + col] = E::cv(v[e]);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            if (row0 + e >= g.r) continue;
+                            const int oi = g.tr ? col : row0 + e, oj = g.tr ? row0 + e : col;
+                            if (a.io_dtype == 0) store_out<0>(a, me, g, oi, oj, v[e]);
+                            else store_out<1>(a, me, g, oi, oj, v[e]);
+                        }
+                    }
+                }
+            }
+}
 
 template <int DT, int MODE>
 __global__ __launch_bounds__(256) void step_gemm_kernel(const StepArgs a) {
@@ -531,81 +614,287 @@ __global__ __launch_bounds__(256) void step_gemm_kernel(const StepArgs a) {
         __syncthreads();
     }
 
-    // ---- epilogue: lane l, register q of block (i,j) holds
-    //      C[m0 + wm*64 + i*32 + rho(l,q)][n0 + wn*64 + j*32 + l%32]; the four
-    //      registers 4m..4m+3 are four consecutive rows, so a transposed
-    //      (mirrored) store writes them as one run ----
-    const float ca = a.abc[3 * a.step], cb = a.abc[3 * a.step + 1], cc = a.abc[3 * a.step + 2];
+    gemm_epilogue<DT, MODE>(a, tref, bm, bn, m0, n0, wm, wn, l32, gl, acc, aval);
+}
+
+// ---------------------------------------------------------------------------
+// bf16 step GEMMs with direct global -> LDS loads (buffer_load ... lds): k
+// chunks of 32 in two LDS stages, the next chunk in flight while one is
+// multiplied.  With no register staging the kernel needs few VGPRs and 32 KB
+// of LDS, so several workgroups share a CU and hide each other's load
+// latency.  Loads are masked through the buffer range: a lane whose 16-byte
+// chunk lies outside the operand (rows past the tile, columns past the row)
+// gets an offset past the buffer's end and reads zeros.  The workspace's row
+// padding (up to a multiple of 8 elements) is kept zero by every writer, so
+// a chunk is either wholly valid or wholly outside.
+// Stage layouts (dense, 16-byte chunks XOR-swizzled by row, so that both the
+// lane-contiguous DMA writes and the MFMA operand reads are conflict free):
+//   row panels (128 rows x 32):  chunk c of row r at position c ^ ((r >> 2) & 3)
+//   X panel of apply (32 x 128): chunk c of row r at position c ^ ((r & 3) * 4)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+template <int MODE>
+__global__ __launch_bounds__(256) void step_gemm_async(const StepArgs a) {
+    using E = Elem<0>;
+    using ET = unsigned short;
+    constexpr int BK = 32;
+    constexpr int STAGE = 128 * BK;                  // elements per operand and stage (8 KB)
+    constexpr bool NN = MODE == 2;
+    __shared__ __attribute__((aligned(16))) ET sbuf[4 * STAGE];   // two stages of P and Q; the C tile
+    ET* const sP0 = sbuf;
+    ET* const sP1 = sbuf + STAGE;
+    ET* const sQ0 = sbuf + 2 * STAGE;
+    ET* const sQ1 = sbuf + 3 * STAGE;
+
+    // ---- workgroup -> (tile, block), blocks of one tile on one XCD ----
+    const int nwg = a.grid_blocks;
+    const int L = (blockIdx.x & 7) * (nwg >> 3) + (blockIdx.x >> 3);
+    const int bpt = NN ? a.nb_max * a.ns_max : a.nb_max * (a.nb_max + 1) / 2;
+    const int tl = L / bpt, b = L - tl * bpt;
+    const int t = a.tile_begin + tl;
+    if (t >= a.tile_end) return;
+    const TileRef tref = find_tile(a, t);
+    const TileGeom& g = tref.g;
+    const int nb = (g.r + 127) / 128, ns = (g.s + 127) / 128;
+    int bm, bn;
+    if (NN) {
+        bm = b / a.ns_max;
+        bn = b - bm * a.ns_max;
+        if (bm >= nb || bn >= ns) return;
+    } else {
+        bm = (int)((sqrtf(8.f * b + 1.f) - 1.f) * 0.5f);
+        while ((bm + 1) * (bm + 2) / 2 <= b) ++bm;
+        while (bm * (bm + 1) / 2 > b) --bm;
+        bn = b - bm * (bm + 1) / 2;
+        if (bm >= nb) return;
+    }
+    const int m0 = bm * 128, n0 = bn * 128;
+
+    const ET* P;
+    const ET* Q;
+    int ldp, ldq, prow, kdim, qrows, qcol;
+    if (MODE == 0) {
+        P = reinterpret_cast<const ET*>(a.Xc) + g.xoff; ldp = (int)round8(g.s);
+        Q = P; ldq = ldp;
+        prow = g.r; kdim = g.s; qrows = g.r; qcol = 0;
+    } else if (MODE == 1) {
+        P = reinterpret_cast<const ET*>(a.A) + g.aoff; ldp = (int)round8(g.r);
+        Q = P; ldq = ldp;
+        prow = g.r; kdim = g.r; qrows = g.r; qcol = 0;
+    } else {
+        P = reinterpret_cast<const ET*>(a.B) + g.aoff; ldp = (int)round8(g.r);
+        Q = reinterpret_cast<const ET*>(a.Xc) + g.xoff; ldq = (int)round8(g.s);
+        prow = g.r; kdim = g.r; qrows = g.r; qcol = g.s;
+    }
+    const uint32_t pbytes = (uint32_t)prow * (uint32_t)ldp * 2u;
+    const uint32_t qbytes = (uint32_t)qrows * (uint32_t)ldq * 2u;
+    const __amdgpu_buffer_rsrc_t rP = rsrc_of(P, pbytes);
+    const __amdgpu_buffer_rsrc_t rQ = rsrc_of(Q, qbytes);
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int l32 = lane & 31, gl = lane >> 5;
+
+    // DMA source of instruction j of this wave (positions (2 wave + j) 64 + lane)
+    int prow_j[2], pcol_j[2], qrow_j[2], qcol_j[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int pos = (wave * 2 + j) * 64 + lane;
+        const int r = pos >> 2;
+        prow_j[j] = r;
+        pcol_j[j] = ((pos & 3) ^ ((r >> 2) & 3)) * 8;
+        if (!NN) {
+            qrow_j[j] = r;
+            qcol_j[j] = pcol_j[j];
+        } else {
+            const int rn = pos >> 4;
+            qrow_j[j] = rn;
+            qcol_j[j] = ((pos & 15) ^ ((rn & 3) * 4)) * 8;
+        }
+    }
+    auto issue = [&](int kt, ET* dP, ET* dQ) __attribute__((always_inline)) {
+        const int k0 = kt * BK;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int pr = m0 + prow_j[j], pk = k0 + pcol_j[j];
+            const uint32_t po = (pr < prow && pk < kdim) ? ((uint32_t)pr * ldp + pk) * 2u : pbytes;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rP, (LDS_AS void*)(dP + (wave * 2 + j) * 512), 16, po, 0, 0, 0);
+            uint32_t qo;
+            if (!NN) {
+                const int qr = n0 + qrow_j[j], qk = k0 + qcol_j[j];
+                qo = (qr < qrows && qk < kdim) ? ((uint32_t)qr * ldq + qk) * 2u : qbytes;
+            } else {
+                const int qr = k0 + qrow_j[j], qc = n0 + qcol_j[j];
+                qo = (qr < kdim && qc < qcol) ? ((uint32_t)qr * ldq + qc) * 2u : qbytes;
+            }
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rQ, (LDS_AS void*)(dQ + (wave * 2 + j) * 512), 16, qo, 0, 0, 0);
+        }
+    };
+
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+    unsigned avp[2][2][8];   // poly: A over the output block, bf16 pairs
+
+    auto compute = [&](int kt, const ET* cP, const ET* cQ) __attribute__((always_inline)) {
+#pragma unroll
+        for (int kk = 0; kk < BK / 16; ++kk) {
+            bf16x8 av[2], bv[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int r = wm * 64 + i * 32 + l32;
+                const int pc = (kk * 2 + gl) ^ ((r >> 2) & 3);
+                av[i] = *reinterpret_cast<const bf16x8*>(&cP[r * BK + pc * 8]);
+            }
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                if (!NN) {
+                    const int r = wn * 64 + j * 32 + l32;
+                    const int pc = (kk * 2 + gl) ^ ((r >> 2) & 3);
+                    bv[j] = *reinterpret_cast<const bf16x8*>(&cQ[r * BK + pc * 8]);
+                } else {
+                    const int G = lane >> 4, i16 = lane & 15;
+                    const int col = wn * 64 + j * 32 + 16 * (G & 1) + 4 * (i16 & 3);
+                    const int row = kk * 16 + 8 * gl + (i16 >> 2);
+                    const int off = row * 128 + (((col >> 3) ^ ((row & 3) * 4)) * 8) + (col & 7);
+                    bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(&cQ[off]));
+                    bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(&cQ[off + 4 * 128]));
+                    bv[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
+        }
+        if constexpr (MODE == 1) {
+            // A over this output block is the k range [n0 + wn 64 + j 32, +32)
+            // of the row panel (A symmetric): one k chunk
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                if (kt == (n0 + wn * 64 + j * 32) / BK) {
+#pragma unroll
+                    for (int i = 0; i < 2; ++i)
+#pragma unroll
+                        for (int q = 0; q < 16; ++q) {
+                            const int r = wm * 64 + i * 32 + (q >> 2) * 8 + gl * 4 + (q & 3);
+                            const int pc = (l32 >> 3) ^ ((r >> 2) & 3);
+                            const unsigned v = cP[r * BK + pc * 8 + (l32 & 7)];
+                            avp[i][j][q >> 1] = (q & 1) ? (avp[i][j][q >> 1] | (v << 16)) : v;
+                        }
+                }
+            }
+        }
+    };
+
+    // ---- pipeline: chunk kt + 1 in flight while kt is multiplied; one barrier
+    //      per chunk (the barrier also tells that every wave is done with the
+    //      stage the next loads overwrite) ----
+    const int nk = (kdim + BK - 1) / BK;
+    issue(0, sP0, sQ0);
+    for (int kt = 0; kt < nk; ++kt) {
+        // every load issued so far (chunk kt) has landed once vmcnt is 0
+        const int cur = kt & 1;
+        __builtin_amdgcn_s_waitcnt(0u | (7u << 4) | (15u << 8));
+        __syncthreads();
+        if (kt + 1 < nk) issue(kt + 1, cur ? sP0 : sP1, cur ? sQ0 : sQ1);
+        compute(kt, cur ? sP1 : sP0, cur ? sQ1 : sQ0);
+    }
+
     const bool last = (MODE == 2) && (a.step == a.K - 1);
-    const MatEntry& me = a.mats[tref.mi];
+    if (last) {
+        // the last update writes the result in place in the data dtype
+        float aval[2][2][16];
+        gemm_epilogue<0, MODE>(a, tref, bm, bn, m0, n0, wm, wn, l32, gl, acc, aval);
+        return;
+    }
+
+    // ---- epilogue through LDS: the 128x128 bf16 block C (row-major, 16-byte
+    //      chunks XOR-swizzled by row), then whole 16-byte row chunks to the
+    //      workspace; the mirrored block of the symmetric products goes the
+    //      same way from C^T ----
+    const float ca = a.abc[3 * a.step], cb = a.abc[3 * a.step + 1], cc = a.abc[3 * a.step + 2];
+    auto sw = [](int row, int col) { return row * 128 + (((col >> 3) ^ (row & 15)) << 3) + (col & 7); };
+    unsigned short cv[2][2][16];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                float v = acc[i][j][q];
+                if constexpr (MODE == 1) {
+                    const float av = (q & 1) ? hi_f(avp[i][j][q >> 1]) : lo_f(avp[i][j][q >> 1]);
+                    v = __builtin_fmaf(cc, v, cb * av);
+                    const int row = m0 + wm * 64 + i * 32 + (q >> 2) * 8 + gl * 4 + (q & 3);
+                    const int col = n0 + wn * 64 + j * 32 + l32;
+                    if (row == col && col < g.r) v += ca;
+                }
+                cv[i][j][q] = f2bf(v);
+            }
+    __syncthreads();   // every wave is done with the k stages
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int q = 0; q < 16; ++q)
+                sbuf[sw(wm * 64 + i * 32 + (q >> 2) * 8 + gl * 4 + (q & 3), wn * 64 + j * 32 + l32)] = cv[i][j][q];
+    __syncthreads();
+    ET* Out;
+    int64_t ldo;
+    int rows_ok, cols_ok;
+    if (MODE == 2) {
+        Out = reinterpret_cast<ET*>(a.Xn) + g.xoff;
+        ldo = round8(g.s);
+        rows_ok = g.r;
+        cols_ok = (int)round8(g.s);
+    } else {
+        Out = reinterpret_cast<ET*>(MODE == 0 ? a.A : a.B) + g.aoff;
+        ldo = round8(g.r);
+        rows_ok = g.r;
+        cols_ok = (int)round8(g.r);   // past r the values are zero: the padding stays zero
+    }
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+        const int id = it * 256 + tid;
+        const int R = id >> 4, ch = id & 15;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(&sbuf[sw(R, ch * 8)]);
+        if (m0 + R < rows_ok && n0 + ch * 8 < cols_ok)
+            *reinterpret_cast<u32x4*>(Out + (int64_t)(m0 + R) * ldo + n0 + ch * 8) = v;
+    }
+    if (MODE == 2 || bm == bn) return;
+    __syncthreads();
+    // C^T: lane l holds rows rho .. rho+3 of column l%32, i.e. 4 consecutive
+    // elements of one row of C^T (8-byte stores)
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
-                const int row0 = m0 + wm * 64 + i * 32 + m * 8 + gl * 4;   // rows row0 .. row0+3
-                const int col = n0 + wn * 64 + j * 32 + l32;
-                float v[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * m + e];
-                if (MODE == 0 || MODE == 1) {
-                    if (col >= g.r) continue;
-                    const int64_t ld = round8(g.r);
-                    ET* Out = reinterpret_cast<ET*>(MODE == 0 ? a.A : a.B) + g.aoff;
-                    if (MODE == 1) {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            if (row0 + e < g.r) {
-                                float bv = __builtin_fmaf(cc, v[e], cb * aval[i][j][4 * m + e]);
-                                if (row0 + e == col) bv += ca;
-                                v[e] = bv;
-                            }
-                        }
-                    }
-                    ET o[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) o[e] = E::cv(v[e]);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (row0 + e < g.r) Out[(int64_t)(row0 + e) * ld + col] = o[e];
-                    if (bm != bn) {
-                        // mirror: row col, columns row0 .. row0+3 (8-aligned rows, so whole runs)
-                        ET* mp = Out + (int64_t)col * ld + row0;
-                        if (row0 + 4 <= g.r) {
-                            if constexpr (DT == 0) {
-                                u32x2 pk = {(unsigned)__builtin_bit_cast(unsigned short, o[0]) |
-                                                ((unsigned)__builtin_bit_cast(unsigned short, o[1]) << 16),
-                                            (unsigned)__builtin_bit_cast(unsigned short, o[2]) |
-                                                ((unsigned)__builtin_bit_cast(unsigned short, o[3]) << 16)};
-                                *reinterpret_cast<u32x2*>(mp) = pk;
-                            } else {
-                                *reinterpret_cast<float4*>(mp) = make_float4(o[0], o[1], o[2], o[3]);
-                            }
-                        } else {
-#pragma unroll
-                            for (int e = 0; e < 4; ++e)
-                                if (row0 + e < g.r) mp[e] = o[e];
-                        }
-                    }
-                } else {
-                    if (col >= g.s) continue;
-                    if (!last) {
-                        ET* Xo = reinterpret_cast<ET*>(a.Xn) + g.xoff;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (row0 + e < g.r) Xo[(int64_t)(row0 + e) * round8(g.s) + col] = E::cv(v[e]);
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            if (row0 + e >= g.r) continue;
-                            const int oi = g.tr ? col : row0 + e, oj = g.tr ? row0 + e : col;
-                            if (a.io_dtype == 0) store_out<0>(a, me, g, oi, oj, v[e]);
-                            else store_out<1>(a, me, g, oi, oj, v[e]);
-                        }
-                    }
-                }
+                const int Rt = wn * 64 + j * 32 + l32;
+                const int Ct = wm * 64 + i * 32 + m * 8 + gl * 4;
+                u32x2 pk = {(unsigned)cv[i][j][4 * m] | ((unsigned)cv[i][j][4 * m + 1] << 16),
+                            (unsigned)cv[i][j][4 * m + 2] | ((unsigned)cv[i][j][4 * m + 3] << 16)};
+                *reinterpret_cast<u32x2*>(&sbuf[sw(Rt, Ct)]) = pk;
             }
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+        const int id = it * 256 + tid;
+        const int R = id >> 4, ch = id & 15;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(&sbuf[sw(R, ch * 8)]);
+        if (n0 + R < rows_ok && m0 + ch * 8 < cols_ok)
+            *reinterpret_cast<u32x4*>(Out + (int64_t)(n0 + R) * ldo + m0 + ch * 8) = v;
+    }
 }
 
 template <int IO, int WK, int PASS>
@@ -631,7 +920,12 @@ hipError_t launch_step_norm(const StepArgs& a, hipStream_t s) {
 template <int MODE>
 static hipError_t launch_gemm(const StepArgs& a, hipStream_t s) {
     if (a.grid_blocks <= 0) return hipSuccess;
-    if (a.wk_dtype == 0)
+    // the direct-to-LDS kernel addresses an operand with 32-bit byte offsets
+    const int64_t rmax = 128LL * a.nb_max, smax = 128LL * a.ns_max;
+    const bool small = rmax * std::max(rmax, smax) * 2 < (1LL << 31);
+    if (a.wk_dtype == 0 && small && HIMUON_STEP_ASYNC)
+        hipLaunchKernelGGL((step_gemm_async<MODE>), dim3(a.grid_blocks), dim3(256), 0, s, a);
+    else if (a.wk_dtype == 0)
         hipLaunchKernelGGL((step_gemm_kernel<0, MODE>), dim3(a.grid_blocks), dim3(256), 0, s, a);
     else
         hipLaunchKernelGGL((step_gemm_kernel<1, MODE>), dim3(a.grid_blocks), dim3(256), 0, s, a);
