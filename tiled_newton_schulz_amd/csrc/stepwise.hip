@@ -809,12 +809,6 @@ __global__ __launch_bounds__(256) void step_gemm_async(const StepArgs a) {
     }
 
     const bool last = (MODE == 2) && (a.step == a.K - 1);
-    if (last) {
-        // the last update writes the result in place in the data dtype
-        float aval[2][2][16];
-        gemm_epilogue<0, MODE>(a, tref, bm, bn, m0, n0, wm, wn, l32, gl, acc, aval);
-        return;
-    }
 
     // ---- epilogue through LDS: the 128x128 bf16 block C (row-major, 16-byte
     //      chunks XOR-swizzled by row), then whole 16-byte row chunks to the
@@ -848,6 +842,57 @@ __global__ __launch_bounds__(256) void step_gemm_async(const StepArgs a) {
             for (int q = 0; q < 16; ++q)
                 sbuf[sw(wm * 64 + i * 32 + (q >> 2) * 8 + gl * 4 + (q & 3), wn * 64 + j * 32 + l32)] = cv[i][j][q];
     __syncthreads();
+    if (MODE == 2 && last) {
+        // the result goes in place into the matrix (bf16), oriented back: a
+        // tall tile was stored transposed, so its C^T block is written; the
+        // Muon variant updates W <- W - eta X instead
+        const MatEntry& me = a.mats[tref.mi];
+        ET* base = reinterpret_cast<ET*>(a.muon ? me.w : me.m);
+        const int64_t ld = a.muon ? me.w_ld : me.m_ld;
+        const bool vec = vec_ok(base, ld, g.c0);
+        if (g.tr) {
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        const int Rt = wn * 64 + j * 32 + l32;
+                        const int Ct = wm * 64 + i * 32 + m * 8 + gl * 4;
+                        u32x2 pk = {(unsigned)cv[i][j][4 * m] | ((unsigned)cv[i][j][4 * m + 1] << 16),
+                                    (unsigned)cv[i][j][4 * m + 2] | ((unsigned)cv[i][j][4 * m + 3] << 16)};
+                        *reinterpret_cast<u32x2*>(&sbuf[sw(Rt, Ct)]) = pk;
+                    }
+            __syncthreads();
+        }
+        // LDS block row R = tile row m0 + R (or, tall, tile column n0 + R)
+        const int rbase = g.tr ? n0 : m0, cbase = g.tr ? m0 : n0;
+#pragma unroll
+        for (int it = 0; it < 8; ++it) {
+            const int id = it * 256 + tid;
+            const int R = id >> 4, ch = id & 15;
+            const int orow = rbase + R, ocol = cbase + ch * 8;
+            if (orow >= g.h || ocol >= g.w) continue;
+            u16x8 v = *reinterpret_cast<const u16x8*>(&sbuf[sw(R, ch * 8)]);
+            ET* op = base + (int64_t)(g.r0 + orow) * ld + g.c0 + ocol;
+            if (vec && ocol + 8 <= g.w) {
+                if (a.muon) {
+                    const u16x8 w0 = *reinterpret_cast<const u16x8*>(op);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) v[e] = f2bf(bf2f(w0[e]) - a.eta * bf2f(v[e]));
+                }
+                *reinterpret_cast<u16x8*>(op) = v;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    if (ocol + e >= g.w) break;
+                    op[e] = a.muon ? f2bf(bf2f(op[e]) - a.eta * bf2f(v[e])) : v[e];
+                }
+            }
+        }
+        return;
+    }
     ET* Out;
     int64_t ldo;
     int rows_ok, cols_ok;
