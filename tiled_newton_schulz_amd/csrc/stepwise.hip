@@ -275,6 +275,9 @@ __device__ __forceinline__ void store_out(const StepArgs& a, const MatEntry& me,
 #ifndef HIMUON_STEP_ASYNC
 #define HIMUON_STEP_ASYNC 1
 #endif
+#ifndef HIMUON_ASYNC_BK
+#define HIMUON_ASYNC_BK 32
+#endif
 // k chunk of the step GEMMs (tuning knobs; multiples of 32)
 #ifndef HIMUON_STEP_BK_BF16
 #define HIMUON_STEP_BK_BF16 64
@@ -640,8 +643,12 @@ template <int MODE>
 __global__ __launch_bounds__(256) void step_gemm_async(const StepArgs a) {
     using E = Elem<0>;
     using ET = unsigned short;
-    constexpr int BK = 32;
-    constexpr int STAGE = 128 * BK;                  // elements per operand and stage (8 KB)
+    constexpr int BK = HIMUON_ASYNC_BK;
+    constexpr int STAGE = 128 * BK;                  // elements per operand and stage
+    constexpr int CPR = BK / 8;                      // 16-byte chunks per panel row
+    constexpr int NPI = CPR / 2;                     // DMA instructions per wave and operand
+    constexpr int SH = CPR == 4 ? 2 : 1;             // row-panel swizzle: chunk ^ ((r >> SH) & (CPR - 1))
+    static_assert(CPR == 4 || CPR == 8, "k chunk of 32 or 64");
     constexpr bool NN = MODE == 2;
     __shared__ __attribute__((aligned(16))) ET sbuf[4 * STAGE];   // two stages of P and Q; the C tile
     ET* const sP0 = sbuf;
@@ -700,13 +707,13 @@ __global__ __launch_bounds__(256) void step_gemm_async(const StepArgs a) {
     const int l32 = lane & 31, gl = lane >> 5;
 
     // DMA source of instruction j of this wave (positions (2 wave + j) 64 + lane)
-    int prow_j[2], pcol_j[2], qrow_j[2], qcol_j[2];
+    int prow_j[NPI], pcol_j[NPI], qrow_j[NPI], qcol_j[NPI];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int pos = (wave * 2 + j) * 64 + lane;
-        const int r = pos >> 2;
+    for (int j = 0; j < NPI; ++j) {
+        const int pos = (wave * NPI + j) * 64 + lane;
+        const int r = pos / CPR;
         prow_j[j] = r;
-        pcol_j[j] = ((pos & 3) ^ ((r >> 2) & 3)) * 8;
+        pcol_j[j] = ((pos % CPR) ^ ((r >> SH) & (CPR - 1))) * 8;
         if (!NN) {
             qrow_j[j] = r;
             qcol_j[j] = pcol_j[j];
@@ -719,10 +726,10 @@ __global__ __launch_bounds__(256) void step_gemm_async(const StepArgs a) {
     auto issue = [&](int kt, ET* dP, ET* dQ) __attribute__((always_inline)) {
         const int k0 = kt * BK;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < NPI; ++j) {
             const int pr = m0 + prow_j[j], pk = k0 + pcol_j[j];
             const uint32_t po = (pr < prow && pk < kdim) ? ((uint32_t)pr * ldp + pk) * 2u : pbytes;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rP, (LDS_AS void*)(dP + (wave * 2 + j) * 512), 16, po, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rP, (LDS_AS void*)(dP + (wave * NPI + j) * 512), 16, po, 0, 0, 0);
             uint32_t qo;
             if (!NN) {
                 const int qr = n0 + qrow_j[j], qk = k0 + qcol_j[j];
@@ -731,7 +738,7 @@ __global__ __launch_bounds__(256) void step_gemm_async(const StepArgs a) {
                 const int qr = k0 + qrow_j[j], qc = n0 + qcol_j[j];
                 qo = (qr < kdim && qc < qcol) ? ((uint32_t)qr * ldq + qc) * 2u : qbytes;
             }
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rQ, (LDS_AS void*)(dQ + (wave * 2 + j) * 512), 16, qo, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rQ, (LDS_AS void*)(dQ + (wave * NPI + j) * 512), 16, qo, 0, 0, 0);
         }
     };
 
@@ -749,14 +756,14 @@ __global__ __launch_bounds__(256) void step_gemm_async(const StepArgs a) {
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
                 const int r = wm * 64 + i * 32 + l32;
-                const int pc = (kk * 2 + gl) ^ ((r >> 2) & 3);
+                const int pc = (kk * 2 + gl) ^ ((r >> SH) & (CPR - 1));
                 av[i] = *reinterpret_cast<const bf16x8*>(&cP[r * BK + pc * 8]);
             }
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 if (!NN) {
                     const int r = wn * 64 + j * 32 + l32;
-                    const int pc = (kk * 2 + gl) ^ ((r >> 2) & 3);
+                    const int pc = (kk * 2 + gl) ^ ((r >> SH) & (CPR - 1));
                     bv[j] = *reinterpret_cast<const bf16x8*>(&cQ[r * BK + pc * 8]);
                 } else {
                     const int G = lane >> 4, i16 = lane & 15;
@@ -779,14 +786,16 @@ __global__ __launch_bounds__(256) void step_gemm_async(const StepArgs a) {
             // of the row panel (A symmetric): one k chunk
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
-                if (kt == (n0 + wn * 64 + j * 32) / BK) {
+                const int c0 = n0 + wn * 64 + j * 32;
+                if (kt == c0 / BK) {
+                    const int cl = c0 - kt * BK + l32;
 #pragma unroll
                     for (int i = 0; i < 2; ++i)
 #pragma unroll
                         for (int q = 0; q < 16; ++q) {
                             const int r = wm * 64 + i * 32 + (q >> 2) * 8 + gl * 4 + (q & 3);
-                            const int pc = (l32 >> 3) ^ ((r >> 2) & 3);
-                            const unsigned v = cP[r * BK + pc * 8 + (l32 & 7)];
+                            const int pc = (cl >> 3) ^ ((r >> SH) & (CPR - 1));
+                            const unsigned v = cP[r * BK + pc * 8 + (cl & 7)];
                             avp[i][j][q >> 1] = (q & 1) ? (avp[i][j][q >> 1] | (v << 16)) : v;
                         }
                 }
