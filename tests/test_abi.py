@@ -155,10 +155,11 @@ def test_plan_moe_ragged_on_chip():
     descs = moe_descs()
     info = H.himuon_plan(descs, 256, 5, H.BF16)
     # 10,240 full tiles and 2,048 ragged 256x128 / 128x256 edge tiles, all on
-    # chip (kernel tile 256), two tile classes per matrix, 256 classes a launch
+    # chip (kernel tile 256): one launch for the 128 interior classes and one
+    # for the 128 narrow edge classes (shorter side <= 128)
     assert info["tiles"] == 64 * 2 * 16 * 6
     assert info["kernel_tile"] == 256 and info["chunks"] == 0 and info["workspace_full"] == 0
-    assert info["resident_launches"] == math.ceil(2 * len(descs) / 256)
+    assert info["resident_launches"] == 2
 
 
 def test_plan_moe_chunking():

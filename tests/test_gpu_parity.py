@@ -106,7 +106,9 @@ def test_bf16_kernel_tile_256_shapes(cuda, T):
     """Tiles whose larger side is 129..256 (zero padded to 256 x 256 on chip),
     including thin, ragged and transposed shapes."""
     rng = np.random.default_rng([25, T])
-    for (h, w) in [(256, 256), (256, 32), (32, 256), (200, 150), (130, 256), (256, 129), (171, 40), (97, 230)]:
+    # (the shorter side <= 128 runs the narrow variant; a tall one is transposed)
+    for (h, w) in [(256, 256), (256, 32), (32, 256), (200, 150), (130, 256), (256, 129), (171, 40), (97, 230),
+                   (128, 256), (256, 128), (129, 128), (128, 129)]:
         x = workloads.round_to(rng.standard_normal((h, w)), "bf16")
         err, _ = full_check(x, T, "bf16")
         say(f"bf16 {h}x{w} T={T}: {err:.3e}")
@@ -247,11 +249,12 @@ def test_chunking_bit_exact(cuda, T, cap_tiles):
 
 
 # ------------------------------------------------------------- Muon step
-@pytest.mark.parametrize("dt,T", [("bf16", 64), ("bf16", 128), ("bf16", 256), ("fp32", 64), ("fp32", 256)])
+@pytest.mark.parametrize("dt,T,shape", [("bf16", 64, (300, 170)), ("bf16", 128, (300, 170)),
+                                        ("bf16", 256, (300, 170)), ("bf16", 256, (250, 100)),
+                                        ("fp32", 64, (300, 170)), ("fp32", 256, (300, 170))])
 @pytest.mark.parametrize("K", [0, 5])
-def test_muon_step(cuda, dt, T, K):
+def test_muon_step(cuda, dt, T, shape, K):
     rng = np.random.default_rng([19, T, K])
-    shape = (300, 170)
     W = workloads.round_to(rng.standard_normal(shape), dt)
     M = workloads.round_to(rng.standard_normal(shape), dt)
     G = workloads.round_to(rng.standard_normal(shape), dt)

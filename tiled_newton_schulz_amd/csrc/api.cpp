@@ -163,6 +163,7 @@ struct Group {
     std::vector<int64_t> tile_base, xoff, aoff;
     int kernel_tile = 0;         // on-chip groups
     bool precise = false;        // on-chip groups
+    bool narrow = false;         // on-chip kernel tile 256: shorter side <= 128
     int wk = 0;                  // step groups: workspace dtype (0 bf16, 1 fp32)
     int64_t tiles = 0;
 };
@@ -198,19 +199,23 @@ himuon_status_t build_plan(const std::vector<MatSpec>& specs, int32_t T, int32_t
 
     // on-chip launches, keyed by (kernel tile, precision)
     for (int precise = 0; precise < 2; ++precise)
-        for (int kt : {32, 64, 128, 256}) {
+        for (int kt : {32, 64, 128, 256})
+          for (int narrow = 0; narrow < (kt == 256 ? 2 : 1); ++narrow) {
             Group cur;
             cur.kernel_tile = kt;
             cur.precise = precise != 0;
+            cur.narrow = narrow != 0;
             for (const TileClass& c : all) {
                 const Route r = route_of(dt, c.th, c.tw);
                 const bool on = precise ? r == Route::OnChipPrecise : r == Route::OnChip;
                 if (!on || kernel_tile_for(c.th, c.tw) != kt) continue;
+                if (kt == 256 && (std::min(c.th, c.tw) <= 128) != (narrow != 0)) continue;
                 if ((int)cur.cls.size() == kGroup || cur.tiles + c.tiles() > INT32_MAX) {
                     plan.rgroups.push_back(cur);
                     cur = Group();
                     cur.kernel_tile = kt;
                     cur.precise = precise != 0;
+                    cur.narrow = narrow != 0;
                 }
                 cur.cls.push_back(c);
                 cur.tile_base.push_back(cur.tiles);
@@ -417,7 +422,7 @@ himuon_status_t run(const std::vector<MatSpec>& specs, int32_t T, int32_t K, con
         const int32_t split = tail_split(G, muon);
         a.tile_begin = 0;
         a.tile_end = split;
-        hipError_t e = launch_resident(a, G.kernel_tile, muon, G.precise, s);
+        hipError_t e = launch_resident(a, G.kernel_tile, muon, G.precise, G.narrow, s);
         if (e != hipSuccess) return hip_fail(e);
         if (split < a.total_tiles) {
             a.tile_begin = split;

@@ -109,9 +109,11 @@ __host__ __device__ inline TileGeom class_tile(const MatEntry& e, int32_t T, int
 }
 
 // Host-side launchers (defined in the .hip files).
-hipError_t launch_resident(const ResidentArgs& a, int kernel_tile, bool muon, bool precise, hipStream_t s);
+// narrow: kernel tile 256 with the shorter tile side <= 128
+hipError_t launch_resident(const ResidentArgs& a, int kernel_tile, bool muon, bool precise, bool narrow,
+                           hipStream_t s);
 hipError_t launch_resident_coop(const ResidentArgs& a, bool muon, hipStream_t s);
-hipError_t launch_resident256(const ResidentArgs& a, bool muon, hipStream_t s);
+hipError_t launch_resident256(const ResidentArgs& a, bool muon, bool narrow, hipStream_t s);
 int resident_slots(int kernel_tile, bool muon, bool precise);   // tiles the device holds at once (0 on error)
 int device_cus();
 hipError_t launch_step_norm(const StepArgs& a, hipStream_t s);

@@ -701,7 +701,8 @@ hipError_t launch_resident_coop(const ResidentArgs& a, bool muon, hipStream_t s)
     return hipGetLastError();
 }
 
-hipError_t launch_resident(const ResidentArgs& a, int kernel_tile, bool muon, bool precise, hipStream_t s) {
+hipError_t launch_resident(const ResidentArgs& a, int kernel_tile, bool muon, bool precise, bool narrow,
+                           hipStream_t s) {
     if (precise) {
         switch (kernel_tile) {
             case 32: return muon ? launch_tk<32, true, true>(a, s) : launch_tk<32, false, true>(a, s);
@@ -713,7 +714,7 @@ hipError_t launch_resident(const ResidentArgs& a, int kernel_tile, bool muon, bo
         case 32: return muon ? launch_tk<32, true, false>(a, s) : launch_tk<32, false, false>(a, s);
         case 64: return muon ? launch_tk<64, true, false>(a, s) : launch_tk<64, false, false>(a, s);
         case 128: return muon ? launch_tk<128, true, false>(a, s) : launch_tk<128, false, false>(a, s);
-        case 256: return launch_resident256(a, muon, s);
+        case 256: return launch_resident256(a, muon, narrow, s);
         default: return hipErrorInvalidValue;
     }
 }

@@ -23,6 +23,12 @@
 // Waves w and w + 4 share a SIMD; the block lists give each SIMD nine of the
 // 36 lower blocks.
 //
+// Narrow tiles (the shorter side 32..128, the longer 129..256) run the same
+// code with NR = 4 row blocks: the tile is oriented so that X has r <= 128
+// rows (a tall tile is transposed on the way into LDS and back on the way out),
+// A and B' are 128 x 128 (10 lower blocks) and X' is r x s; this does about a
+// quarter of the padded 256 x 256 work.
+//
 // Register layouts as in the kernel-tile-128 kernel: AL (accumulator layout)
 // lane l, register q holds M[rho(l,q)][l % 32], rho = (q/4)*8 + (l/32)*4 + q%4;
 // RL = AL of the transpose.
@@ -33,19 +39,45 @@ namespace himuon {
 
 namespace {
 
-constexpr int kT = 256, kLD = kT + 8, kNB = 8;
+constexpr int kT = 256, kLD = kT + 8;
 
-// Lower 32x32 blocks (i, j), i >= j, of a symmetric 256 x 256 product, per wave.
-constexpr int kBlkN[8] = {4, 4, 4, 4, 5, 5, 5, 5};
-constexpr int kBlkI[8][5] = {{2, 2, 3, 3, 0}, {4, 4, 5, 5, 0}, {6, 6, 7, 7, 0}, {4, 4, 5, 5, 0},
-                             {6, 6, 7, 7, 0}, {6, 6, 7, 7, 1}, {1, 2, 3, 3, 4}, {5, 5, 6, 7, 7}};
-constexpr int kBlkJ[8][5] = {{0, 1, 0, 1, 0}, {0, 1, 0, 1, 0}, {0, 1, 0, 1, 0}, {2, 3, 2, 3, 0},
-                             {2, 3, 2, 3, 0}, {4, 5, 4, 5, 1}, {0, 2, 2, 3, 4}, {4, 5, 6, 6, 7}};
+// Lower 32x32 blocks (i, j), i >= j, of a symmetric product with NR x NR
+// blocks, per wave (at most five).
+template <int NR> struct Blocks;
+template <> struct Blocks<8> {
+    static constexpr int n[8] = {4, 4, 4, 4, 5, 5, 5, 5};
+    static constexpr int i[8][5] = {{2, 2, 3, 3, 0}, {4, 4, 5, 5, 0}, {6, 6, 7, 7, 0}, {4, 4, 5, 5, 0},
+                                    {6, 6, 7, 7, 0}, {6, 6, 7, 7, 1}, {1, 2, 3, 3, 4}, {5, 5, 6, 7, 7}};
+    static constexpr int j[8][5] = {{0, 1, 0, 1, 0}, {0, 1, 0, 1, 0}, {0, 1, 0, 1, 0}, {2, 3, 2, 3, 0},
+                                    {2, 3, 2, 3, 0}, {4, 5, 4, 5, 1}, {0, 2, 2, 3, 4}, {4, 5, 6, 6, 7}};
+};
+template <> struct Blocks<4> {
+    static constexpr int n[8] = {2, 2, 2, 2, 1, 1, 0, 0};
+    static constexpr int i[8][5] = {{1, 0}, {2, 1}, {3, 2}, {2, 3}, {3}, {3}, {}, {}};
+    static constexpr int j[8][5] = {{0, 0}, {0, 1}, {0, 2}, {1, 3}, {1}, {2}, {}, {}};
+};
 
+template <int NR>
 constexpr bool uses_row(int w, int r) {
-    for (int b = 0; b < kBlkN[w]; ++b)
-        if (kBlkI[w][b] == r || kBlkJ[w][b] == r) return true;
+    for (int b = 0; b < Blocks<NR>::n[w]; ++b)
+        if (Blocks<NR>::i[w][b] == r || Blocks<NR>::j[w][b] == r) return true;
     return false;
+}
+
+template <int N> struct IC { static constexpr int value = N; };
+// Runs f(IC<w>) for the wave index w (uniform, in a scalar register).
+template <class F>
+__device__ __forceinline__ void per_wave(int w, F&& f) {
+    switch (w) {
+        case 0: f(IC<0>{}); break;
+        case 1: f(IC<1>{}); break;
+        case 2: f(IC<2>{}); break;
+        case 3: f(IC<3>{}); break;
+        case 4: f(IC<4>{}); break;
+        case 5: f(IC<5>{}); break;
+        case 6: f(IC<6>{}); break;
+        default: f(IC<7>{}); break;
+    }
 }
 
 // LDS pointers with the lane-dependent part of each access pattern folded in,
@@ -70,30 +102,33 @@ __device__ __forceinline__ u32x4 col_frag(const LdsLanes& L, int k0, int c0) {
     return __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// Lower blocks of M M^T (M the LDS matrix) for wave W, accumulated in AL.
-template <int W>
+// Lower blocks of M M^T (M the LDS matrix, KC k chunks of 16) for wave W,
+// accumulated in AL.
+template <int NR, int KC, int W>
 __device__ __forceinline__ void gram_lower(const LdsLanes& L, f32x16 (&acc)[5]) {
+    using B = Blocks<NR>;
 #pragma unroll
     for (int b = 0; b < 5; ++b) acc[b] = f32x16{};
 #pragma unroll
-    for (int kc = 0; kc < kT / 16; ++kc) {
-        u32x4 rf[kNB];
+    for (int kc = 0; kc < KC; ++kc) {
+        u32x4 rf[NR];
 #pragma unroll
-        for (int r = 0; r < kNB; ++r)
-            if (uses_row(W, r)) rf[r] = row_frag(L, r, kc * 16);
+        for (int r = 0; r < NR; ++r)
+            if (uses_row<NR>(W, r)) rf[r] = row_frag(L, r, kc * 16);
 #pragma unroll
-        for (int b = 0; b < kBlkN[W]; ++b) acc[b] = mfma32w(rf[kBlkI[W][b]], rf[kBlkJ[W][b]], acc[b]);
+        for (int b = 0; b < B::n[W]; ++b) acc[b] = mfma32w(rf[B::i[W][b]], rf[B::j[W][b]], acc[b]);
     }
 }
 
 // Writes the wave's lower blocks (bf16 AL in p) into the LDS matrix as a full
 // symmetric matrix: block (j, i) from the row layout (8-byte stores), block
 // (i, j) for i != j from AL (2-byte stores).
-template <int W>
+template <int NR, int W>
 __device__ __forceinline__ void store_sym(const LdsLanes& L, const u32x4 (&p)[5][2]) {
+    using B = Blocks<NR>;
 #pragma unroll
-    for (int b = 0; b < kBlkN[W]; ++b) {
-        const int i = kBlkI[W][b], j = kBlkJ[W][b];
+    for (int b = 0; b < B::n[W]; ++b) {
+        const int i = B::i[W][b], j = B::j[W][b];
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             u32x2 v = {p[b][m >> 1][2 * (m & 1)], p[b][m >> 1][2 * (m & 1) + 1]};
@@ -111,11 +146,12 @@ __device__ __forceinline__ void store_sym(const LdsLanes& L, const u32x4 (&p)[5]
 }
 
 // B' = c A^2 + b A (+ a on the diagonal), in place of the rounded A in p.
-template <int W>
+template <int NR, int W>
 __device__ __forceinline__ void combine(f32x16 (&acc)[5], u32x4 (&p)[5][2], float ca, float cb, float cc,
                                         int l32, int g) {
+    using B = Blocks<NR>;
 #pragma unroll
-    for (int b = 0; b < kBlkN[W]; ++b) {
+    for (int b = 0; b < B::n[W]; ++b) {
 #pragma unroll
         for (int f = 0; f < 2; ++f)
 #pragma unroll
@@ -124,7 +160,7 @@ __device__ __forceinline__ void combine(f32x16 (&acc)[5], u32x4 (&p)[5][2], floa
                 acc[b][e] = __builtin_fmaf(cc, acc[b][e], cb * lo_f(p[b][f][k]));
                 acc[b][e + 1] = __builtin_fmaf(cc, acc[b][e + 1], cb * hi_f(p[b][f][k]));
             }
-        if (kBlkI[W][b] == kBlkJ[W][b]) {
+        if (B::i[W][b] == B::j[W][b]) {
 #pragma unroll
             for (int q = 0; q < 16; ++q)
                 if ((q >> 2) * 8 + g * 4 + (q & 3) == l32) acc[b][q] += ca;
@@ -134,24 +170,12 @@ __device__ __forceinline__ void combine(f32x16 (&acc)[5], u32x4 (&p)[5][2], floa
     }
 }
 
-// Runs F<w>(args...) for the wave index w (uniform, in a scalar register).
-#define HIMUON_PER_WAVE(w, F, ...)           \
-    switch (w) {                             \
-        case 0: F<0>(__VA_ARGS__); break;    \
-        case 1: F<1>(__VA_ARGS__); break;    \
-        case 2: F<2>(__VA_ARGS__); break;    \
-        case 3: F<3>(__VA_ARGS__); break;    \
-        case 4: F<4>(__VA_ARGS__); break;    \
-        case 5: F<5>(__VA_ARGS__); break;    \
-        case 6: F<6>(__VA_ARGS__); break;    \
-        default: F<7>(__VA_ARGS__); break;   \
-    }
-
 }  // namespace
 
-template <bool MUON>
+template <bool MUON, int NR>
 __global__ __launch_bounds__(512) void resident256_kernel(const ResidentArgs args) {
-    __shared__ __attribute__((aligned(16))) unsigned short sX[kT * kLD];
+    constexpr int XR = NR * 32;                     // rows of X in LDS
+    __shared__ __attribute__((aligned(16))) unsigned short sX[XR * kLD];
     __shared__ float red[8];
 
     const int tid = threadIdx.x;
@@ -163,10 +187,15 @@ __global__ __launch_bounds__(512) void resident256_kernel(const ResidentArgs arg
     const MatEntry& me = args.mats[find_class(args.mats, args.nmats, t)];
     const TileGeom tg = class_tile(me, args.T, t - me.tile_base);
     const int h = tg.h, wd = tg.w;
+    // X is the tile itself, or (a tall narrow tile) its transpose
+    const bool tr = NR == 4 && h > wd;
     unsigned short* mbase = reinterpret_cast<unsigned short*>(me.m) + (int64_t)tg.r0 * me.m_ld + tg.c0;
     const bool mvec = vec_ok(me.m, me.m_ld, tg.c0);
     using IO = TileIO<kT>;
-    constexpr int NCH = kT * IO::CPR / 512;   // 16-byte chunks per thread
+    // 16-byte chunks of the tile per thread: XR rows of 32 chunks, or (tall)
+    // 256 rows of 16
+    constexpr int NCH = XR * 32 / 512;
+    const int cpr = tr ? 16 : 32;
 
     // ---- load (Muon: M <- mu M + G, stored) into LDS, sum of squares ----
     {
@@ -180,7 +209,7 @@ __global__ __launch_bounds__(512) void resident256_kernel(const ResidentArgs arg
 #pragma unroll 4
         for (int it = 0; it < NCH; ++it) {
             const int idx = it * 512 + tid;
-            const int r = idx / IO::CPR, col = (idx % IO::CPR) * 8;
+            const int r = idx / cpr, col = (idx % cpr) * 8;
             u16x8 v = IO::load(mbase, me.m_ld, r, col, h, wd, mvec);
             if constexpr (MUON) {
                 u16x8 gv = IO::load(gbase, me.g_ld, r, col, h, wd, gvec);
@@ -190,7 +219,12 @@ __global__ __launch_bounds__(512) void resident256_kernel(const ResidentArgs arg
             }
 #pragma unroll
             for (int e = 0; e < 8; ++e) { const float x = bf2f(v[e]); ss = __builtin_fmaf(x, x, ss); }
-            *reinterpret_cast<u16x8*>(&sX[r * kLD + col]) = v;
+            if (!tr) {
+                *reinterpret_cast<u16x8*>(&sX[r * kLD + col]) = v;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) sX[(col + e) * kLD + r] = v[e];
+            }
         }
         ss = wave_sum(ss);
         if (lane == 0) red[w] = ss;
@@ -199,11 +233,10 @@ __global__ __launch_bounds__(512) void resident256_kernel(const ResidentArgs arg
 #pragma unroll
         for (int i = 0; i < 8; ++i) tot += red[i];
         const float scale = 1.0f / (sqrtf(tot) + args.eps);
-        // each thread rescales the chunks it wrote
 #pragma unroll 4
         for (int it = 0; it < NCH; ++it) {
             const int idx = it * 512 + tid;
-            const int r = idx / IO::CPR, col = (idx % IO::CPR) * 8;
+            const int r = idx >> 5, col = (idx & 31) * 8;
             u16x8 v = *reinterpret_cast<const u16x8*>(&sX[r * kLD + col]);
 #pragma unroll
             for (int e = 0; e < 8; ++e) v[e] = f2bf(bf2f(v[e]) * scale);
@@ -225,11 +258,12 @@ __global__ __launch_bounds__(512) void resident256_kernel(const ResidentArgs arg
         const LdsLanes L{sX + o_rf, sX + o_cf, sX + o_rl, sX + o_al};
         f32x16 acc[5];
         u32x4 p[5][2];
-        // 1. lower blocks of A = X X^T; this wave's column block of X
-        HIMUON_PER_WAVE(w, gram_lower, L, acc);
-        u32x4 xf[kNB][2];
+        // 1. lower blocks of A = X X^T (k over the 256 columns); this wave's
+        //    column block of X
+        per_wave(w, [&](auto W) { gram_lower<NR, kT / 16, decltype(W)::value>(L, acc); });
+        u32x4 xf[NR][2];
 #pragma unroll
-        for (int K = 0; K < kNB; ++K)
+        for (int K = 0; K < NR; ++K)
 #pragma unroll
             for (int kc = 0; kc < 2; ++kc) xf[K][kc] = col_frag(L, K * 32 + kc * 16, w * 32);
 #pragma unroll
@@ -239,21 +273,24 @@ __global__ __launch_bounds__(512) void resident256_kernel(const ResidentArgs arg
         }
         __syncthreads();
         // 2. A over X
-        HIMUON_PER_WAVE(w, store_sym, L, p);
+        per_wave(w, [&](auto W) { store_sym<NR, decltype(W)::value>(L, p); });
         __syncthreads();
-        // 3. A^2 = A A^T, B' = a I + b A + c A^2, B' over A
-        HIMUON_PER_WAVE(w, gram_lower, L, acc);
-        HIMUON_PER_WAVE(w, combine, acc, p, ca, cb, cc, l32, g);
+        // 3. A^2 = A A^T (k over the XR columns of A), B' = a I + b A + c A^2,
+        //    B' over A
+        per_wave(w, [&](auto W) {
+            gram_lower<NR, XR / 16, decltype(W)::value>(L, acc);
+            combine<NR, decltype(W)::value>(acc, p, ca, cb, cc, l32, g);
+        });
         __syncthreads();
-        HIMUON_PER_WAVE(w, store_sym, L, p);
+        per_wave(w, [&](auto W) { store_sym<NR, decltype(W)::value>(L, p); });
         __syncthreads();
         // 4. X'^T(w, I) = sum_K X(K, w)^T B'(K, I), two row blocks I at a time
-        u32x4 xo[kNB][2];
+        u32x4 xo[NR][2];
 #pragma unroll
-        for (int I = 0; I < kNB; I += 2) {
+        for (int I = 0; I < NR; I += 2) {
             f32x16 c0 = {}, c1 = {};
 #pragma unroll
-            for (int K = 0; K < kNB; ++K)
+            for (int K = 0; K < NR; ++K)
 #pragma unroll
                 for (int kc = 0; kc < 2; ++kc) {
                     const int k0 = K * 32 + kc * 16;
@@ -268,7 +305,7 @@ __global__ __launch_bounds__(512) void resident256_kernel(const ResidentArgs arg
         __syncthreads();
         // X' over B': RL(X'(I, w)) -> row I*32 + l%32, columns w*32 + rho
 #pragma unroll
-        for (int I = 0; I < kNB; ++I)
+        for (int I = 0; I < NR; ++I)
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
                 u32x2 v = {xo[I][m >> 1][2 * (m & 1)], xo[I][m >> 1][2 * (m & 1) + 1]};
@@ -277,7 +314,8 @@ __global__ __launch_bounds__(512) void resident256_kernel(const ResidentArgs arg
         __syncthreads();
     }
 
-    // ---- write back in place (Muon: W <- W - eta X) ----
+    // ---- write back in place (Muon: W <- W - eta X), transposed back for a
+    //      tall tile ----
     unsigned short* obase = mbase;
     int64_t old = me.m_ld;
     bool ovec = mvec;
@@ -289,8 +327,14 @@ __global__ __launch_bounds__(512) void resident256_kernel(const ResidentArgs arg
 #pragma unroll
     for (int it = 0; it < NCH; ++it) {
         const int idx = it * 512 + tid;
-        const int r = idx / IO::CPR, col = (idx % IO::CPR) * 8;
-        u16x8 v = *reinterpret_cast<const u16x8*>(&sX[r * kLD + col]);
+        const int r = idx / cpr, col = (idx % cpr) * 8;
+        u16x8 v;
+        if (!tr) {
+            v = *reinterpret_cast<const u16x8*>(&sX[r * kLD + col]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = sX[(col + e) * kLD + r];
+        }
         if constexpr (MUON) {
             u16x8 wv = IO::load(obase, old, r, col, h, wd, ovec);
 #pragma unroll
@@ -300,13 +344,20 @@ __global__ __launch_bounds__(512) void resident256_kernel(const ResidentArgs arg
     }
 }
 
-hipError_t launch_resident256(const ResidentArgs& a, bool muon, hipStream_t s) {
+hipError_t launch_resident256(const ResidentArgs& a, bool muon, bool narrow, hipStream_t s) {
     const int n = a.tile_end - a.tile_begin;
     if (n <= 0) return hipSuccess;
-    if (muon)
-        hipLaunchKernelGGL((resident256_kernel<true>), dim3(n), dim3(512), 0, s, a);
-    else
-        hipLaunchKernelGGL((resident256_kernel<false>), dim3(n), dim3(512), 0, s, a);
+    if (narrow) {
+        if (muon)
+            hipLaunchKernelGGL((resident256_kernel<true, 4>), dim3(n), dim3(512), 0, s, a);
+        else
+            hipLaunchKernelGGL((resident256_kernel<false, 4>), dim3(n), dim3(512), 0, s, a);
+    } else {
+        if (muon)
+            hipLaunchKernelGGL((resident256_kernel<true, 8>), dim3(n), dim3(512), 0, s, a);
+        else
+            hipLaunchKernelGGL((resident256_kernel<false, 8>), dim3(n), dim3(512), 0, s, a);
+    }
     return hipGetLastError();
 }
 
