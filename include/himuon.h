@@ -136,6 +136,28 @@ himuon_status_t himuon_tiled_ns(const himuon_matrix_t* m, int32_t n, int32_t T, 
                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * himuon_tiled_ns_schedule - K Newton-Schulz steps with a tile size per step:
+ * step k works on the T[k] x T[k] tiles (HiMuon abstract, "runtime tile-size
+ * schedules", read as a per-step tile size).  Each tile of the first size is
+ * normalised once (eps added to its Frobenius norm); later steps use the
+ * tiles as they stand.  The sizes must not increase and each must divide the
+ * one before, so a finer tile lies inside one coarser tile; the step count of
+ * a size and its coefficients are taken in order from abc (3 K floats, host).
+ * Steps of one size run as one himuon_tiled_ns pass; between passes the
+ * matrices hold the current iterate in their own dtype.
+ *
+ * Arguments as for himuon_tiled_ns, with T a host array of K tile sizes.
+ * workspace_bytes caps every pass; the workspace must fit the largest need of
+ * any pass (himuon_workspace_size for that pass's tile size).
+ * Errors: HIMUON_ERR_INVALID_ARGUMENT for K < 1 or > HIMUON_MAX_STEPS, a
+ * null T, a size < 1, or sizes that increase or do not nest; otherwise as for
+ * himuon_tiled_ns.  Every pass is validated before the first is enqueued.
+ */
+himuon_status_t himuon_tiled_ns_schedule(const himuon_matrix_t* m, int32_t n, const int32_t* T, int32_t K,
+                                         const float* abc, himuon_dtype_t dt, float eps, void* workspace,
+                                         size_t workspace_bytes, void* stream);
+
+/*
  * himuon_muon_step - fused Muon update with the tiled map in place of polar()
  * ("Gram Newton-Schulz" summary page, section 3, the Muon update rule):
  *     M <- mu M + G            (stored back into M, rounded to dt)

@@ -247,3 +247,22 @@ def test_routes_in_plan():
     # T = 16: every tile is 16 x 16 and runs on chip with hi/lo splitting
     info = H.himuon_plan([sd(64, 64)], 16, 5, H.BF16)
     assert info["tiles"] == 16 and info["resident_launches"] == 1 and info["kernel_tile"] == 32
+
+
+def test_schedule_validation():
+    """The per-step tile-size schedule rejects sizes that increase or do not
+    nest, K outside 1..16 and a null size array, before any launch."""
+    d = (H.himuon_matrix_t * 1)(sd(600, 520))
+    abc = H.coeff_array((3.4445, -4.775, 2.0315), 3)
+    f = H.lib.himuon_tiled_ns_schedule
+
+    def ts(*v):
+        return (ctypes.c_int32 * len(v))(*v)
+
+    assert f(d, 1, ts(256, 512, 512), 3, abc, H.BF16, 1e-7, None, 0, None) == 1   # increasing
+    assert f(d, 1, ts(256, 96, 32), 3, abc, H.BF16, 1e-7, None, 0, None) == 1     # 96 does not divide 256
+    assert f(d, 1, ts(256, 128, 0), 3, abc, H.BF16, 1e-7, None, 0, None) == 1     # size < 1
+    assert f(d, 1, ts(256), 0, abc, H.BF16, 1e-7, None, 0, None) == 1             # K = 0
+    assert f(d, 1, None, 3, abc, H.BF16, 1e-7, None, 0, None) == 1                # no sizes
+    # a pass that needs a workspace (T = 512: step path) without one
+    assert f(d, 1, ts(512, 256, 128), 3, abc, H.BF16, 1e-7, None, 0, None) == 5

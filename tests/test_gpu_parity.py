@@ -368,3 +368,51 @@ def test_tail_split_bit_exact(cuda):
         single = b.clone()
         run([single], 128)
         assert torch.equal(single, m)
+
+
+# ------------------------------------------------------------- tile-size schedule
+@pytest.mark.parametrize("dt,Ts", [("bf16", [512, 256, 128, 64, 64]), ("bf16", [256, 256, 128, 128, 32]),
+                                   ("fp32", [256, 128, 64])])
+def test_tile_size_schedule(cuda, dt, Ts):
+    """Per-step tile sizes inside one call against the oracle's schedule."""
+    rng = np.random.default_rng([28, len(Ts), Ts[0]])
+    x = workloads.round_to(rng.standard_normal((600, 520)), dt)
+    abc = MIXED[:len(Ts)]
+    ref = oracle.tiled_ns_schedule(x.double().numpy(), Ts, abc)
+    g = x.cuda()
+    H.himuon_tiled_ns_schedule([g], Ts, abc)
+    torch.cuda.synchronize()
+    err = oracle.tile_rel_errors(to_np(g), ref, Ts[0]).max()
+    say(f"{dt} schedule {Ts}: {err:.3e}")
+    assert err <= TOL[dt]
+
+
+def test_schedule_of_one_size_is_the_plain_map(cuda):
+    rng = np.random.default_rng(29)
+    x = workloads.round_to(rng.standard_normal((300, 700)), "bf16").cuda()
+    a, b = x.clone(), x.clone()
+    H.himuon_tiled_ns([a], 128, 5, MIXED)
+    H.himuon_tiled_ns_schedule([b], [128] * 5, MIXED)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_dense8192_schedule(cuda):
+    """The dense layer with the per-step schedule 512, 256, 128, 128, 128 under
+    the 4 GiB cap; sampled 512-tiles checked with the oracle's schedule (a
+    512-tile's result depends on that tile alone)."""
+    w = WORKLOADS["dense8192"]
+    mats = workloads.device_tensors(w)
+    Ts = [512, 256, 128, 128, 128]
+    rng = np.random.default_rng(30)
+    sampled = grab(mats, 512, 4, rng)
+    H.himuon_tiled_ns_schedule(mats, Ts, COEFFS, workspace_bytes=4 << 30)
+    torch.cuda.synchronize()
+    worst = 0.0
+    for mi, ti, tj, tile in sampled:
+        ref = oracle.tiled_ns_schedule(tile, Ts, COEFFS)
+        h, w_ = tile.shape
+        got = to_np(mats[mi][ti * 512:ti * 512 + h, tj * 512:tj * 512 + w_])
+        worst = max(worst, oracle.tile_rel_errors(got, ref, 512).max())
+    say(f"dense8192 schedule: {len(sampled)} tiles, max err {worst:.3e}")
+    assert worst <= TOL["bf16"]

@@ -20,8 +20,8 @@ MAX_STEPS = 16
 
 STATUS = {0: "HIMUON_OK", 1: "HIMUON_ERR_INVALID_ARGUMENT", 2: "HIMUON_ERR_UNSUPPORTED",
           3: "HIMUON_ERR_LAYOUT", 4: "HIMUON_ERR_OVERLAP", 5: "HIMUON_ERR_WORKSPACE", 6: "HIMUON_ERR_HIP"}
-EXPORTS = ["himuon_plan", "himuon_workspace_size", "himuon_tiled_ns", "himuon_muon_step",
-           "himuon_status_string", "himuon_last_hip_error", "himuon_version"]
+EXPORTS = ["himuon_plan", "himuon_workspace_size", "himuon_tiled_ns", "himuon_tiled_ns_schedule",
+           "himuon_muon_step", "himuon_status_string", "himuon_last_hip_error", "himuon_version"]
 
 
 class himuon_matrix_t(ctypes.Structure):
@@ -61,6 +61,10 @@ def _load():
                                   P(ctypes.c_float), ctypes.c_int, ctypes.c_float, ctypes.c_void_p,
                                   ctypes.c_size_t, ctypes.c_void_p]
     L.himuon_tiled_ns.restype = ctypes.c_int
+    L.himuon_tiled_ns_schedule.argtypes = [P(himuon_matrix_t), ctypes.c_int32, P(ctypes.c_int32), ctypes.c_int32,
+                                           P(ctypes.c_float), ctypes.c_int, ctypes.c_float, ctypes.c_void_p,
+                                           ctypes.c_size_t, ctypes.c_void_p]
+    L.himuon_tiled_ns_schedule.restype = ctypes.c_int
     L.himuon_muon_step.argtypes = [P(himuon_matrix_t), P(himuon_matrix_t), P(himuon_matrix_t), ctypes.c_int32,
                                    ctypes.c_int32, ctypes.c_int32, P(ctypes.c_float), ctypes.c_float,
                                    ctypes.c_float, ctypes.c_int, ctypes.c_float, ctypes.c_void_p,
@@ -193,6 +197,32 @@ def himuon_tiled_ns(mats: Sequence, T: int, K: int, abc=(3.4445, -4.7750, 2.0315
                                ctypes.c_void_p(ptr), nbytes, _stream_handle(stream))
     _check(code, "himuon_tiled_ns")
     return ws
+
+
+def himuon_tiled_ns_schedule(mats: Sequence, Ts: Sequence[int], abc=(3.4445, -4.7750, 2.0315), eps: float = 1e-7,
+                             workspace=None, workspace_bytes: int | None = None, stream=None):
+    """len(Ts) Newton-Schulz steps in place, step k on the Ts[k] x Ts[k] tiles
+    (non-increasing, nested sizes; one normalisation, on the first size)."""
+    if len(mats) == 0:
+        return
+    dtype = _dtype_code(mats[0])
+    d = _descs(mats)
+    K = len(Ts)
+    ts = (ctypes.c_int32 * max(1, K))(*[int(t) for t in Ts])
+    if workspace is None:
+        # the largest need of any pass, capped
+        need = max(himuon_workspace_size(mats, int(t), dtype)[0] for t in set(Ts)) if K else 0
+        if need:
+            import torch
+            need = need if workspace_bytes is None else max(min(need, workspace_bytes), 0)
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=mats[0].device)
+            workspace_bytes = need
+    ptr = workspace.data_ptr() if workspace is not None else None
+    nbytes = 0 if workspace is None else (workspace.numel() if workspace_bytes is None else workspace_bytes)
+    code = lib.himuon_tiled_ns_schedule(d, len(mats), ts, K, coeff_array(abc, K), dtype, eps,
+                                        ctypes.c_void_p(ptr), nbytes, _stream_handle(stream))
+    _check(code, "himuon_tiled_ns_schedule")
+    return workspace
 
 
 def himuon_muon_step(W: Sequence, M: Sequence, G: Sequence, T: int, K: int, abc=(3.4445, -4.7750, 2.0315),

@@ -395,7 +395,7 @@ himuon_status_t hip_fail(hipError_t e) {
 
 himuon_status_t run(const std::vector<MatSpec>& specs, int32_t T, int32_t K, const float* abc,
                     himuon_dtype_t dt, float eps, float mu, float eta, bool muon, void* ws, size_t ws_bytes,
-                    void* stream) {
+                    void* stream, bool normalize = true) {
     if (specs.empty()) return HIMUON_OK;
     if (ws_bytes > 0 && ws == nullptr) return HIMUON_ERR_WORKSPACE;
     Plan plan;
@@ -414,6 +414,7 @@ himuon_status_t run(const std::vector<MatSpec>& specs, int32_t T, int32_t K, con
         a.T = T;
         a.K = K;
         a.eps = eps;
+        a.normalize = normalize ? 1 : 0;
         a.mu = mu;
         a.eta = eta;
         // Tiles beyond the last full round of one-wave tiles go to the
@@ -452,6 +453,7 @@ himuon_status_t run(const std::vector<MatSpec>& specs, int32_t T, int32_t K, con
         a.wk_dtype = G.wk;
         a.muon = muon ? 1 : 0;
         a.eps = eps;
+        a.normalize = normalize ? 1 : 0;
         a.mu = mu;
         a.eta = eta;
         char* base = reinterpret_cast<char*>(ws);
@@ -533,6 +535,43 @@ himuon_status_t himuon_tiled_ns(const himuon_matrix_t* m, int32_t n, int32_t T, 
     std::vector<MatSpec> specs;
     if ((st = gather(nullptr, m, nullptr, n, T, dt, specs)) != HIMUON_OK) return st;
     return run(specs, T, K, abc, dt, eps, 0.f, 0.f, false, workspace, workspace_bytes, stream);
+}
+
+himuon_status_t himuon_tiled_ns_schedule(const himuon_matrix_t* m, int32_t n, const int32_t* T, int32_t K,
+                                         const float* abc, himuon_dtype_t dt, float eps, void* workspace,
+                                         size_t workspace_bytes, void* stream) {
+    if (K < 1 || K > HIMUON_MAX_STEPS || T == nullptr) return HIMUON_ERR_INVALID_ARGUMENT;
+    for (int k = 0; k < K; ++k) {
+        if (T[k] < 1) return HIMUON_ERR_INVALID_ARGUMENT;
+        if (k > 0 && (T[k] > T[k - 1] || T[k - 1] % T[k] != 0)) return HIMUON_ERR_INVALID_ARGUMENT;
+    }
+    himuon_status_t st = check_common(n, T[0], K, dt, eps);
+    if (st != HIMUON_OK) return st;
+    if ((st = check_abc(K, abc)) != HIMUON_OK) return st;
+    // validate every run (tile size) before enqueueing anything
+    std::vector<std::vector<MatSpec>> runs;
+    std::vector<int32_t> run_T, run_k0, run_K;
+    for (int k = 0; k < K;) {
+        int k1 = k;
+        while (k1 < K && T[k1] == T[k]) ++k1;
+        std::vector<MatSpec> specs;
+        if ((st = check_common(n, T[k], k1 - k, dt, eps)) != HIMUON_OK) return st;
+        if ((st = gather(nullptr, m, nullptr, n, T[k], dt, specs)) != HIMUON_OK) return st;
+        Plan plan;
+        if ((st = build_plan(specs, T[k], k1 - k, dt, workspace_bytes, true, plan)) != HIMUON_OK) return st;
+        if (!plan.chunks.empty() && workspace == nullptr) return HIMUON_ERR_WORKSPACE;
+        runs.push_back(std::move(specs));
+        run_T.push_back(T[k]);
+        run_k0.push_back(k);
+        run_K.push_back(k1 - k);
+        k = k1;
+    }
+    for (size_t i = 0; i < runs.size(); ++i) {
+        st = run(runs[i], run_T[i], run_K[i], abc + 3 * run_k0[i], dt, eps, 0.f, 0.f, false, workspace,
+                 workspace_bytes, stream, i == 0);
+        if (st != HIMUON_OK) return st;
+    }
+    return HIMUON_OK;
 }
 
 himuon_status_t himuon_muon_step(const himuon_matrix_t* W, const himuon_matrix_t* M, const himuon_matrix_t* G,

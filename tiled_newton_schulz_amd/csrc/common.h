@@ -39,6 +39,7 @@ struct ResidentArgs {
     int32_t K;
     float eps;
     float mu, eta;       // Muon step only
+    int32_t normalize;   // 0: the tiles are used as they are (later runs of a tile-size schedule)
 };
 
 // Arguments of the step-by-step path kernels for one chunk of tiles.
@@ -60,6 +61,7 @@ struct StepArgs {
     int32_t wk_dtype;           // workspace: 0 bf16, 1 fp32
     int32_t muon;
     float eps, mu, eta;
+    int32_t normalize;          // 0: the tiles are used as they are (later runs of a tile-size schedule)
     void* Xc;                   // oriented tiles, current step
     void* Xn;                   // oriented tiles, next step
     void* A;                    // Gram matrices A = X X^T

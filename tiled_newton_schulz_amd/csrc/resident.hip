@@ -102,7 +102,7 @@ __global__ __launch_bounds__(64) void resident_kernel(const ResidentArgs args) {
         }
     }
     ss = wave_sum(ss);
-    const float scale = 1.0f / (sqrtf(ss) + args.eps);
+    const float scale = args.normalize ? 1.0f / (sqrtf(ss) + args.eps) : 1.0f;
 
     // RL run (block I,J; run m = q/4): row I*32 + l32, cols J*32 + 8m + 4g .. +3
     auto rl_off = [&](int I, int J, int m) { return (I * 32 + l32) * LD + J * 32 + 8 * m + 4 * g; };
@@ -530,7 +530,7 @@ __global__ __launch_bounds__(512) void resident_coop_kernel(const ResidentArgs a
         if (lane == 0) red[0] = ss;
     }
     __syncthreads();
-    const float scale = 1.0f / (sqrtf(red[0]) + args.eps);
+    const float scale = args.normalize ? 1.0f / (sqrtf(red[0]) + args.eps) : 1.0f;
 #pragma unroll
     for (int it = 0; it < NCH; ++it) {
         const int idx = it * 512 + tid;

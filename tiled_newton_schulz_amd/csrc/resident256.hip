@@ -232,7 +232,7 @@ __global__ __launch_bounds__(512) void resident256_kernel(const ResidentArgs arg
         float tot = 0.f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) tot += red[i];
-        const float scale = 1.0f / (sqrtf(tot) + args.eps);
+        const float scale = args.normalize ? 1.0f / (sqrtf(tot) + args.eps) : 1.0f;
 #pragma unroll 4
         for (int it = 0; it < NCH; ++it) {
             const int idx = it * 512 + tid;

@@ -177,7 +177,7 @@ __global__ __launch_bounds__(256) void step_norm_kernel(const StepArgs a) {
 
     float tot = 0.f;
     for (int i = 0; i < a.wg_norm; ++i) tot += a.partial[(int64_t)tl * a.wg_norm + i];
-    const float scale = 1.0f / (sqrtf(tot) + a.eps);
+    const float scale = a.normalize ? 1.0f / (sqrtf(tot) + a.eps) : 1.0f;
     WT* xo = reinterpret_cast<WT*>(a.Xc) + g.xoff;
     const int64_t xld = round8(g.s);
     ET* wbase = a.muon ? reinterpret_cast<ET*>(me.w) + (int64_t)g.r0 * me.w_ld + g.c0 : nullptr;
