@@ -174,6 +174,9 @@ def main():
     ap.add_argument("--T", type=int, default=None)
     ap.add_argument("--K", type=int, default=5)
     ap.add_argument("--cap", type=int, default=None, help="workspace cap in bytes")
+    ap.add_argument("--schedule", default=None,
+                    help="per-step tile sizes, e.g. 512,256,128,128,128 (non-increasing, nested); "
+                         "replaces --T and --K")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB, 5 times (used to "
@@ -220,8 +223,20 @@ def main():
     plan = H.himuon_plan(mats, T, K, H.BF16 if w.dtype == "bf16" else H.FP32, ws_bytes)
     stream = torch.cuda.current_stream()
 
+    sched = [int(x) for x in args.schedule.split(",")] if args.schedule else None
+    if sched:
+        T, K = sched[0], len(sched)
+        need = max(H.himuon_workspace_size(mats, t)[0] for t in set(sched))
+        ws_bytes = min(need, cap) if cap else need
+        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev) if ws_bytes else None
+        plan = H.himuon_plan(mats, sched[-1], 0, H.BF16 if w.dtype == "bf16" else H.FP32, ws_bytes)
+
     def step():
-        H.himuon_tiled_ns(mats, T, K, workloads.COEFFS, workspace=ws, workspace_bytes=ws_bytes, stream=stream)
+        if sched:
+            H.himuon_tiled_ns_schedule(mats, sched, workloads.COEFFS, workspace=ws, workspace_bytes=ws_bytes,
+                                       stream=stream)
+        else:
+            H.himuon_tiled_ns(mats, T, K, workloads.COEFFS, workspace=ws, workspace_bytes=ws_bytes, stream=stream)
 
     for _ in range(args.warmup):
         step()
@@ -238,12 +253,21 @@ def main():
     gpu_ms = ev0.elapsed_time(ev1)
     ms_per_step = gpu_ms / args.steps
 
-    nominal = sum(6.0 * h * ww * T * K for h, ww in shapes)
-    alg = algorithmic_flops(shapes, T, K)
+    if sched:
+        nominal = sum(6.0 * h * ww * t for h, ww in shapes for t in sched)
+        alg = sum(algorithmic_flops(shapes, t, 1) for t in sched)
+    else:
+        nominal = sum(6.0 * h * ww * T * K for h, ww in shapes)
+        alg = algorithmic_flops(shapes, T, K)
     tflops = nominal / (ms_per_step * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
-    roof = dominant_kernel_roofline(H, torch, mats, shapes, T, K, plan, stream, ms_per_step, alg, peak,
-                                    w, args.steps)
+    if sched:
+        roof = {"bound": "mfma", "achieved": round(alg / (ms_per_step * 1e-3) / 1e12, 3), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(alg / (ms_per_step * 1e-3) / 1e12 / peak, 4), "traffic": None,
+                "kernel": "whole schedule", "tiles": None, "launch_ms": round(ms_per_step, 5)}
+    else:
+        roof = dominant_kernel_roofline(H, torch, mats, shapes, T, K, plan, stream, ms_per_step, alg, peak,
+                                        w, args.steps)
     io_bytes = 2.0 * sum(h * ww for h, ww in shapes) * (2 if w.dtype == "bf16" else 4)
     out = {
         "metric": METRIC,
@@ -258,7 +282,7 @@ def main():
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic (seeded normal entries, transformer-layer shapes)",
-        "config": {"workload": w.name, "matrices": len(shapes), "T": T, "K": K,
+        "config": {"workload": w.name, "matrices": len(shapes), "T": sched if sched else T, "K": K,
                    "elements": sum(h * ww for h, ww in shapes), "launches_per_step": plan["launches"],
                    "tiles": plan["tiles"], "tail_tiles": plan["tail_tiles"], "chunks": plan["chunks"],
                    "workspace_bytes": ws_bytes, "parallelism": "single GPU"},
@@ -269,7 +293,7 @@ def main():
         "wall_ms_per_step": round(wall * 1e3 / args.steps, 5),
         "roofline": roof,
     }
-    if not args.no_cpu:
+    if not args.no_cpu and not sched:
         out["cpu_baseline"] = cpu_baseline(w, T, K)
     print(json.dumps(out), flush=True)
 
