@@ -274,24 +274,26 @@ __global__ __launch_bounds__(64) void resident_kernel(const ResidentArgs args) {
         if constexpr (SYM) {
             // lower blocks (P >= Q), two chains at a time; the kernel tile 128
             // path folds a X into the product: B' = a I + B (a added after
-            // the fma, so that c = 0 is handled too)
+            // the fma, so that c = 0 is handled too).  Software pipelined: the
+            // products of the next pair are issued before this pair's epilogue
+            // (VALU) and transposes, so the two overlap.
             constexpr int NL = NB * (NB + 1) / 2;
-#pragma unroll
-            for (int p = 0; p < NL; p += 2) {
+            constexpr int NP = (NL + 1) / 2;
+            auto blk = [](int idx, int& P, int& Q) {
+                int c = 0;
+                for (int i = 0; i < NB; ++i)
+                    for (int j = 0; j <= i; ++j) {
+                        if (c == idx) { P = i; Q = j; }
+                        ++c;
+                    }
+            };
+            auto products = [&](int p, f32x16& a1, f32x16& a2) __attribute__((always_inline)) {
                 int P1 = 0, Q1 = 0, P2 = 0, Q2 = 0;
-                {
-                    int c = 0;
-#pragma unroll
-                    for (int i = 0; i < NB; ++i)
-#pragma unroll
-                        for (int j = 0; j <= i; ++j) {
-                            if (c == p) { P1 = i; Q1 = j; }
-                            if (c == p + 1) { P2 = i; Q2 = j; }
-                            ++c;
-                        }
-                }
-                const bool two = p + 1 < NL;
-                f32x16 a1 = {}, a2 = {};
+                blk(2 * p, P1, Q1);
+                blk(2 * p + 1, P2, Q2);
+                const bool two = 2 * p + 1 < NL;
+                a1 = f32x16{};
+                a2 = f32x16{};
 #pragma unroll
                 for (int K = 0; K < NB; ++K)
 #pragma unroll
@@ -299,6 +301,17 @@ __global__ __launch_bounds__(64) void resident_kernel(const ResidentArgs args) {
                         a1 = mfma32w(Abf[K][P1][f], Abf[K][Q1][f], a1);
                         if (two) a2 = mfma32w(Abf[K][P2][f], Abf[K][Q2][f], a2);
                     }
+            };
+            f32x16 c1, c2;
+            products(0, c1, c2);
+#pragma unroll
+            for (int p = 0; p < NP; ++p) {
+                int P1 = 0, Q1 = 0, P2 = 0, Q2 = 0;
+                blk(2 * p, P1, Q1);
+                blk(2 * p + 1, P2, Q2);
+                const bool two = 2 * p + 1 < NL;
+                f32x16 a1 = c1, a2 = c2;
+                if (p + 1 < NP) products(p + 1, c1, c2);
 #pragma unroll
                 for (int f = 0; f < 2; ++f)
 #pragma unroll
