@@ -603,6 +603,6 @@ const char* himuon_status_string(himuon_status_t s) {
 
 int32_t himuon_last_hip_error(void) { return g_last_hip; }
 
-int32_t himuon_version(void) { return 10000; }
+int32_t himuon_version(void) { return 10100; }
 
 }  // extern "C"

@@ -13,6 +13,10 @@
 // squares (fixed partition and order, so the result is deterministic) and
 // write the normalised, oriented tiles.
 //
+// bf16 workspaces use step_gemm_async (global -> LDS by buffer_load ... lds,
+// epilogue through LDS); fp32 workspaces and operands of 2 GiB or more use
+// step_gemm_kernel (register-staged loads, element-wise stores).
+//
 // Workgroup -> (tile, block) ids are remapped so that the blocks of one tile
 // run on one XCD and share its L2.
 
