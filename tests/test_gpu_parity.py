@@ -416,3 +416,25 @@ def test_dense8192_schedule(cuda):
         worst = max(worst, oracle.tile_rel_errors(got, ref, 512).max())
     say(f"dense8192 schedule: {len(sampled)} tiles, max err {worst:.3e}")
     assert worst <= TOL["bf16"]
+
+
+# ------------------------------------------------------------- error tails
+@pytest.mark.parametrize("T,N", [(32, 48), (64, 48), (128, 24)])
+def test_error_tail_over_many_tiles(cuda, T, N):
+    """Worst per-tile error over tens of thousands of random bf16 tiles (N
+    matrices of 1024 x 1024, every tile checked with the batched oracle): the
+    sampled workload tests do not reach the tail of the error distribution."""
+    gen = torch.Generator(device="cuda").manual_seed(31 + T)
+    mats = [torch.randn(1024, 1024, device="cuda", generator=gen).to(torch.bfloat16) for _ in range(N)]
+    nt = 1024 // T
+
+    def tiles_of(ms):
+        a = np.stack([to_np(m) for m in ms])
+        return a.reshape(N, nt, T, nt, T).transpose(0, 1, 3, 2, 4).reshape(-1, T, T)
+
+    ref = oracle.ns_map_stack(tiles_of(mats), COEFFS, K=5)
+    run(mats, T)
+    got = tiles_of(mats)
+    err = np.linalg.norm((got - ref).reshape(len(ref), -1), axis=1) / np.linalg.norm(ref.reshape(len(ref), -1), axis=1)
+    say(f"T={T}: {len(err)} tiles, worst {err.max():.3e}, mean {err.mean():.3e}")
+    assert err.max() <= TOL["bf16"]

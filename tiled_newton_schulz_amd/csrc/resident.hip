@@ -27,12 +27,13 @@
 // kernel rounds it the same way.
 //
 // Precision (bf16 MFMA operands, fp32 accumulation):
-//  * kernel tiles 32 and 64 keep the tile in fp32 registers; X' = a X starts
-//    from fp32 and X is rounded to bf16 only as an MFMA operand.  Kernel tile
-//    32 also carries B as a bf16 hi/lo pair (B X = B_hi X + B_lo X).
-//  * kernel tile 128 keeps the tile in LDS as bf16 and folds a X into the
-//    product, X' = (a I + B) X, equal in exact arithmetic, with a added to the
-//    diagonal of B before it is rounded.
+//  * kernel tile 32 keeps the tile in fp32 registers; X' = a X starts from
+//    fp32 and X is rounded to bf16 only as an MFMA operand; B is carried as a
+//    bf16 hi/lo pair (B X = B_hi X + B_lo X).
+//  * kernel tiles 64 and 128 keep the tile in LDS as bf16, compute only the
+//    lower blocks of A and A^2, and fold a X into the product,
+//    X' = (a I + B) X, equal in exact arithmetic, with a added to the diagonal
+//    of B before it is rounded.
 //  * PRECISE (tiles with a side below 32, where bf16 rounding of a small
 //    Gram matrix dominates): X, A and B all carried as bf16 hi/lo pairs, three
 //    products per contraction (the lo x lo term dropped).
@@ -45,7 +46,11 @@ template <int TK, bool MUON, bool PRECISE>
 __global__ __launch_bounds__(64) void resident_kernel(const ResidentArgs args) {
     constexpr int NB = TK / 32;          // 32x32 blocks per side
     constexpr int LD = TK + 8;           // LDS row stride (elements), 16-byte pad
-    constexpr bool MASTER32 = TK <= 64;  // fp32 copy of the tile in registers
+    // fp32 copy of the tile in registers for kernel tile 32 and the split
+    // precision; kernel tiles 64 and 128 keep the tile in bf16 (measured over
+    // 12k random 64-tiles: 1.68e-2 worst, against 1.86e-2 with the fp32 copy;
+    // 32-tiles in bf16 reach 2.9e-2, too close to the 3e-2 bound)
+    constexpr bool MASTER32 = TK <= 32 || PRECISE;
     constexpr bool SPLIT_X = PRECISE;
     constexpr bool SPLIT_A = PRECISE;
     constexpr bool SPLIT_B = PRECISE || TK == 32;
@@ -54,7 +59,7 @@ __global__ __launch_bounds__(64) void resident_kernel(const ResidentArgs args) {
 
     __shared__ __attribute__((aligned(16))) unsigned short sX[TK * LD];
     __shared__ __attribute__((aligned(16))) unsigned short sXl[SPLIT_X ? TK * LD : 8];
-    // Kernel tile 128 computes only the lower 32x32 blocks of the symmetric
+    // Kernel tiles 64 and 128 compute only the lower 32x32 blocks of the symmetric
     // products A and A^2; an upper block is the transpose of a lower one and is
     // made by staging the lower block in LDS as its transpose and reading it
     // back with ds_read_tr16_b64.
@@ -272,9 +277,9 @@ __global__ __launch_bounds__(64) void resident_kernel(const ResidentArgs args) {
 
         // B = b A + c A^2 (A symmetric: AL(A(K,P)) is the row operand of A(P,K))
         if constexpr (SYM) {
-            // lower blocks (P >= Q), two chains at a time; the kernel tile 128
-            // path folds a X into the product: B' = a I + B (a added after
-            // the fma, so that c = 0 is handled too).  Software pipelined: the
+            // lower blocks (P >= Q), two chains at a time; a X is folded into
+            // the product: B' = a I + B (a added after the fma, so that c = 0
+            // is handled too).  Software pipelined: the
             // products of the next pair are issued before this pair's epilogue
             // (VALU) and transposes, so the two overlap.
             constexpr int NL = NB * (NB + 1) / 2;
