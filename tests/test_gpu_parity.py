@@ -370,6 +370,27 @@ def test_tail_split_bit_exact(cuda):
         assert torch.equal(single, m)
 
 
+def test_grid_stride_ragged_mix_bit_exact(cuda):
+    """More kernel-tile-128 tiles than the device holds at once (1,875), full
+    and ragged tile classes mixed: each workgroup then walks several tiles,
+    loading the next full tile during the last step of the current one.
+    Matrix-by-matrix calls (at most 256 tiles each) run one tile per
+    workgroup.  The arithmetic is the same, so the results are equal bit for
+    bit."""
+    rng = np.random.default_rng([43, 1])
+    shapes = [(2048, 2048), (1000, 1500), (2048, 2048), (300, 2100), (2048, 2048), (2048, 700),
+              (2048, 2048), (1500, 1000), (2048, 2048), (2048, 2048)]
+    base = [workloads.round_to(rng.standard_normal(s), "bf16").cuda() for s in shapes]
+    batched = [b.clone() for b in base]
+    say("batched call, 1,875 tiles of 128")
+    run(batched, 128)
+    for i, (b, m) in enumerate(zip(base, batched)):
+        single = b.clone()
+        say(f"single call {i}: {tuple(b.shape)}")
+        run([single], 128)
+        assert torch.equal(single, m), i
+
+
 # ------------------------------------------------------------- tile-size schedule
 @pytest.mark.parametrize("dt,Ts", [("bf16", [512, 256, 128, 64, 64]), ("bf16", [256, 256, 128, 128, 32]),
                                    ("fp32", [256, 128, 64])])

@@ -38,7 +38,15 @@
 //    Gram matrix dominates): X, A and B all carried as bf16 hi/lo pairs, three
 //    products per contraction (the lo x lo term dropped).
 
+#include <atomic>
+
 #include "device_util.h"
+
+// Grid-stride launch of the kernel-tile-128 map, with each tile's load
+// overlapped with the step before (0: one workgroup per tile).
+#ifndef HIMUON_PERSIST128
+#define HIMUON_PERSIST128 1
+#endif
 
 namespace himuon {
 
@@ -56,6 +64,13 @@ __global__ __launch_bounds__(64) void resident_kernel(const ResidentArgs args) {
     constexpr bool SPLIT_B = PRECISE || TK == 32;
     static_assert(!PRECISE || MASTER32, "hi/lo splitting needs the fp32 tile");
     using IO = TileIO<TK>;
+    // Kernel tile 128 (plain map) is launched with at most one workgroup per
+    // resident slot and walks its tiles with a grid stride.  The next tile is
+    // loaded into registers before the last step of the current one, and the
+    // stores of a tile drain while the next one starts, so that a wave's tile
+    // I/O overlaps MFMA work instead of every wave of a round loading (and
+    // storing) at the same time.
+    constexpr bool PERSIST = TK == 128 && !MUON && !PRECISE && HIMUON_PERSIST128;
 
     __shared__ __attribute__((aligned(16))) unsigned short sX[TK * LD];
     __shared__ __attribute__((aligned(16))) unsigned short sXl[SPLIT_X ? TK * LD : 8];
@@ -67,12 +82,20 @@ __global__ __launch_bounds__(64) void resident_kernel(const ResidentArgs args) {
     constexpr int LDT = 40;   // staging row stride (elements)
     __shared__ __attribute__((aligned(16))) unsigned short sT[SYM ? 2 * 32 * LDT : 8];
 
-    const int lane = threadIdx.x;
+    u16x8 chunk[IO::NCH];   // the tile as loaded: bf16 16-byte chunks, row-major order
+    bool loaded = false;    // chunk already holds tile t (loaded during the tile before)
+    int t = args.tile_begin + blockIdx.x;
+    for (;;) {
+    // the lane index is hidden from the optimiser once per tile, so that lane
+    // dependent LDS addresses are formed where they are used rather than kept
+    // in registers across the tile loop
+    int lane_v = threadIdx.x;
+    if constexpr (PERSIST) asm volatile("" : "+v"(lane_v));
+    const int lane = lane_v;
     const int l32 = lane & 31;
     const int g = lane >> 5;
 
     // ---- which tile: class by scalar scan of the launch table ----
-    const int t = args.tile_begin + blockIdx.x;
     const MatEntry& me = args.mats[find_class(args.mats, args.nmats, t)];
     const TileGeom tg = class_tile(me, args.T, t - me.tile_base);
     const int r0 = tg.r0, c0 = tg.c0, h = tg.h, w = tg.w;
@@ -82,7 +105,6 @@ __global__ __launch_bounds__(64) void resident_kernel(const ResidentArgs args) {
 
     // ---- load (Muon: M <- mu M + G, stored), sum of squares ----
     float ss = 0.f;
-    u16x8 chunk[IO::NCH];
     {
         const unsigned short* gbase = nullptr;
         bool gvec = false;
@@ -90,21 +112,25 @@ __global__ __launch_bounds__(64) void resident_kernel(const ResidentArgs args) {
             gbase = reinterpret_cast<const unsigned short*>(me.g) + (int64_t)r0 * me.g_ld + c0;
             gvec = vec_ok(me.g, me.g_ld, c0);
         }
+        if (!PERSIST || !loaded) {
 #pragma unroll
-        for (int it = 0; it < IO::NCH; ++it) {
-            const int idx = it * 64 + lane;
-            const int r = idx / IO::CPR, col = (idx % IO::CPR) * 8;
-            u16x8 v = IO::load(mbase, me.m_ld, r, col, h, w, mvec);
-            if constexpr (MUON) {
-                u16x8 gv = IO::load(gbase, me.g_ld, r, col, h, w, gvec);
+            for (int it = 0; it < IO::NCH; ++it) {
+                const int idx = it * 64 + lane;
+                const int r = idx / IO::CPR, col = (idx % IO::CPR) * 8;
+                u16x8 v = IO::load(mbase, me.m_ld, r, col, h, w, mvec);
+                if constexpr (MUON) {
+                    u16x8 gv = IO::load(gbase, me.g_ld, r, col, h, w, gvec);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) v[e] = f2bf(args.mu * bf2f(v[e]) + bf2f(gv[e]));
-                IO::store(mbase, me.m_ld, r, col, h, w, mvec, v);
+                    for (int e = 0; e < 8; ++e) v[e] = f2bf(args.mu * bf2f(v[e]) + bf2f(gv[e]));
+                    IO::store(mbase, me.m_ld, r, col, h, w, mvec, v);
+                }
+                chunk[it] = v;
             }
-            chunk[it] = v;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) { float x = bf2f(v[e]); ss = __builtin_fmaf(x, x, ss); }
         }
+#pragma unroll
+        for (int it = 0; it < IO::NCH; ++it)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) { float x = bf2f(chunk[it][e]); ss = __builtin_fmaf(x, x, ss); }
     }
     ss = wave_sum(ss);
     const float scale = args.normalize ? 1.0f / (sqrtf(ss) + args.eps) : 1.0f;
@@ -182,7 +208,10 @@ __global__ __launch_bounds__(64) void resident_kernel(const ResidentArgs args) {
     }
 
     // ---- K Newton-Schulz steps ----
-    for (int step = 0; step < args.K; ++step) {
+    const int tn = t + (int)gridDim.x;
+    const bool next = PERSIST && tn < args.tile_end;
+    // before_apply runs between B' and the X' product (the prefetch hook)
+    auto ns_step = [&](int step, auto before_apply) __attribute__((always_inline)) {
         const float ca = args.abc[3 * step], cb = args.abc[3 * step + 1], cc = args.abc[3 * step + 2];
         u32x4 Abf[NB][NB][2];                       // AL(A), bf16 (hi)
         u32x4 Alo[SPLIT_A ? NB : 1][SPLIT_A ? NB : 1][2];
@@ -389,6 +418,8 @@ __global__ __launch_bounds__(64) void resident_kernel(const ResidentArgs args) {
             }
         }
 
+        // (B' of the last block pair is an input, so the hook stays after B')
+        before_apply(Bbf[NB - 1][NB - 1][1][3]);
         // X' = a X + B X, computed as X'^T blocks so the result lands in RL
 #pragma unroll
         for (int J = 0; J < NB; ++J) {
@@ -432,6 +463,41 @@ __global__ __launch_bounds__(64) void resident_kernel(const ResidentArgs args) {
             }
         }
         __syncthreads();
+    };
+    auto no_hook = [](unsigned) {};
+    // The next tile's data, in flight during the last X' product and the
+    // stores, when it is a full aligned tile (ragged tiles are loaded at the
+    // top of their own iteration).  chunk is assigned on both paths, so that
+    // the previous tile's data is not kept live across the steps.
+    bool pre = false;
+    auto prefetch = [&](unsigned after) {
+        if (next) {
+            const MatEntry& mn = args.mats[find_class(args.mats, args.nmats, tn)];
+            const TileGeom tgn = class_tile(mn, args.T, tn - mn.tile_base);
+            const unsigned short* nbase =
+                reinterpret_cast<const unsigned short*>(mn.m) + (int64_t)tgn.r0 * mn.m_ld + tgn.c0;
+            pre = tgn.h == TK && tgn.w == TK && vec_ok(mn.m, mn.m_ld, tgn.c0);
+            if (pre) {
+                // chunk it of a lane: row RPI it + lane / CPR, columns 8 (lane % CPR) .. + 7
+                constexpr int RPI = 64 / IO::CPR;
+                int64_t off = (int64_t)(lane / IO::CPR) * mn.m_ld + (lane % IO::CPR) * 8;
+                asm volatile("" : "+v"(off) : "v"(after));
+                const unsigned short* p = nbase + off;
+#pragma unroll
+                for (int it = 0; it < IO::NCH; ++it)
+                    chunk[it] = *reinterpret_cast<const u16x8*>(p + (int64_t)(RPI * it) * mn.m_ld);
+                return;
+            }
+        }
+#pragma unroll
+        for (int it = 0; it < IO::NCH; ++it) chunk[it] = u16x8{};
+    };
+    if constexpr (PERSIST) {
+        for (int step = 0; step < args.K - 1; ++step) ns_step(step, no_hook);
+        if (args.K > 0) ns_step(args.K - 1, prefetch);
+        else prefetch(0u);
+    } else {
+        for (int step = 0; step < args.K; ++step) ns_step(step, no_hook);
     }
 
     // ---- write back in place (Muon: W <- W - eta X) ----
@@ -468,6 +534,10 @@ __global__ __launch_bounds__(64) void resident_kernel(const ResidentArgs args) {
             }
             IO::store(obase, old, r, col, h, w, ovec, v);
         }
+    }
+    if (!next) break;
+    t = tn;
+    loaded = pre;
     }
 }
 
@@ -677,19 +747,38 @@ __global__ __launch_bounds__(512) void resident_coop_kernel(const ResidentArgs a
 }
 
 template <int TK, bool MUON, bool PRECISE>
-static hipError_t launch_tk(const ResidentArgs& a, hipStream_t s) {
-    const int n = a.tile_end - a.tile_begin;
-    if (n <= 0) return hipSuccess;
-    hipLaunchKernelGGL((resident_kernel<TK, MUON, PRECISE>), dim3(n), dim3(64), 0, s, a);
-    return hipGetLastError();
-}
-
-template <int TK, bool MUON, bool PRECISE>
 static int slots_tk() {
     int per_cu = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, resident_kernel<TK, MUON, PRECISE>, 64, 0) != hipSuccess)
         return 0;
     return per_cu * device_cus();
+}
+
+// Resident slots of the grid-stride (kernel tile 128) kernel on the current
+// device, cached per device; 0 if unknown (then one workgroup per tile).
+static int persist_slots() {
+    static std::atomic<int> cache[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v == 0) {
+        v = slots_tk<128, false, false>();
+        cache[dev].store(v, std::memory_order_relaxed);
+    }
+    return v > 0 ? v : 0;
+}
+
+template <int TK, bool MUON, bool PRECISE>
+static hipError_t launch_tk(const ResidentArgs& a, hipStream_t s) {
+    const int n = a.tile_end - a.tile_begin;
+    if (n <= 0) return hipSuccess;
+    int grid = n;
+    if constexpr (TK == 128 && !MUON && !PRECISE && HIMUON_PERSIST128) {
+        const int slots = persist_slots();
+        if (slots > 0 && slots < n) grid = slots;
+    }
+    hipLaunchKernelGGL((resident_kernel<TK, MUON, PRECISE>), dim3(grid), dim3(64), 0, s, a);
+    return hipGetLastError();
 }
 
 int device_cus() {
