@@ -31,6 +31,10 @@ Readings of points the pages leave open (each is listed in the design doc):
 * epsilon is added to the norm, not to its square;
 * the pages give no numeric (a, b, c); callers pass one triple per step.
 
+The submodule ``oracle.diagnostics`` holds the tiled-versus-full-map measures
+(distance, cosine, output spectrum), pinned by
+``tests/test_oracle_diagnostics.py``.
+
 Parity status: every function below is pinned by ``tests/test_oracle.py``
 (SVD closed form, independent full-matrix form, exact rational brute force,
 tile independence, transpose symmetry, zero padding, closed forms for rank-1,
@@ -52,3 +56,4 @@ from .tiled_ns import (  # noqa: F401
     algorithmic_flops,
     nominal_flops,
 )
+from . import diagnostics  # noqa: F401,E402
