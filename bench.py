@@ -80,6 +80,7 @@ def cpu_baseline(w, T, K, min_seconds=10.0, max_seconds=30.0):
 KERNEL_SOURCES = {
     "resident_kernel<128>": ["resident.hip", "device_util.h", "common.h"],
     "resident256_kernel": ["resident256.hip", "device_util.h", "common.h"],
+    "pair_stats": ["pair_stats.hip", "pair_stats.h"],
 }
 KERNEL_OF_TILE = {128: "resident_kernel<128>", 256: "resident256_kernel"}
 
@@ -160,6 +161,61 @@ def dominant_kernel_roofline(H, torch, mats, shapes, T, K, plan, stream, ms_per_
             "launch_ms": round(ms, 5)}
 
 
+def pair_stats_bench(H, torch, w, mats, steps, warmup, no_cpu):
+    """Time himuon_pair_stats over (matrix, copy) pairs of the workload: the
+    three sums behind the tiled-versus-full distance and cosine.  A step is
+    one call (per-workgroup partials, then the fixed-order finish); it reads
+    every element of both matrices once, so the bound is HBM bandwidth."""
+    a = mats
+    b = [m.clone() for m in mats]
+    es = 2 if w.dtype == "bf16" else 4
+    nbytes = 2.0 * sum(m.numel() for m in mats) * es
+    out = torch.empty((len(a), 3), dtype=torch.float64, device=a[0].device)
+    ws = torch.empty(max(H.himuon_pair_stats_workspace(a), 8), dtype=torch.uint8, device=a[0].device)
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        H.himuon_pair_stats(a, b, out=out, workspace=ws, stream=stream)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(steps):
+        H.himuon_pair_stats(a, b, out=out, workspace=ws, stream=stream)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / steps
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    res = {
+        "metric": "pair statistics GB/s (both matrices read once)",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic (seeded normal entries, transformer-layer shapes)",
+        "config": {"workload": w.name + " pair statistics", "pairs": len(a),
+                   "elements": sum(m.numel() for m in mats), "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs / PEAK_HBM_GBS, 4),
+                     "traffic": recorded_traffic("pair_stats", w.name, None, len(a)),
+                     "kernel": "pair_partial_kernel + pair_final_kernel (whole call)", "launch_ms": round(ms, 5)},
+    }
+    if not no_cpu:
+        import numpy as np
+
+        from oracle import diagnostics as OD
+        hx = [m.cpu().to(torch.float64).numpy() for m in mats[:2]]
+        hy = [x.copy() for x in hx]
+        n_el, t0, reps = 0, time.perf_counter(), 0
+        while time.perf_counter() - t0 < 10.0 or reps == 0:
+            for x, y in zip(hx, hy):
+                OD.pair_stats(x, y)
+                n_el += x.size
+            reps += 1
+        dt = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": round(2.0 * n_el * es / dt / 1e9, 2), "unit": "GB/s (same byte count)",
+                               "cores": 1, "kind": "oracle",
+                               "sample": f"oracle pair_stats on the first {len(hx)} matrices, {reps} passes"}
+        del np
+    return res
+
+
 def w_coeffs():
     import workloads
     return workloads.COEFFS
@@ -178,6 +234,8 @@ def main():
                     help="per-step tile sizes, e.g. 512,256,128,128,128 (non-increasing, nested); "
                          "replaces --T and --K")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--pair-stats", action="store_true",
+                    help="time the pair statistics (tiled-versus-full diagnostics) instead of the map")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB, 5 times (used to "
                          "calibrate the HBM byte counters)")
@@ -213,6 +271,9 @@ def main():
     else:
         mats = [t.to(dev) for t in workloads.host_tensors(w)]
     shapes = [tuple(m.shape) for m in mats]
+    if args.pair_stats:
+        print(json.dumps(pair_stats_bench(H, torch, w, mats, args.steps, args.warmup, args.no_cpu)), flush=True)
+        return
     cap = args.cap if args.cap is not None else w.workspace_cap
     full, mn = H.himuon_workspace_size(mats, T)
     ws = None

@@ -174,6 +174,41 @@ himuon_status_t himuon_muon_step(const himuon_matrix_t* W, const himuon_matrix_t
                                  const float* abc, float mu, float eta, himuon_dtype_t dt,
                                  float eps, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * himuon_pair_stats - for n pairs of equal-shaped matrices (a[i], b[i]) the
+ * three sums  sum a*b,  sum a*a,  sum b*b  over all elements, in fp64.
+ *
+ * They measure how far a tiled Newton-Schulz output lies from the
+ * full-matrix map of the same input (HiMuon abstract: the tiled map acts on
+ * each tile alone, where the full map couples all rows and columns; the pages
+ * give no measure of that gap).  With g = tiled, f = full:
+ *     ||g - f||_F / ||f||_F = sqrt(gg + ff - 2 gf) / sqrt(ff),
+ *     cosine = gf / sqrt(gg ff).
+ *
+ * a, b     : n descriptors each (host arrays, read during the call); a[i] and
+ *            b[i] must have equal rows and cols (their ld may differ).  Read
+ *            only; they may overlap each other.
+ * dt       : element type of every matrix.
+ * out      : device array of 3 n doubles, written (out[3i .. 3i+2] =
+ *            sum a*b, sum a*a, sum b*b of pair i); 8-byte aligned.
+ * workspace, workspace_bytes : device scratch for per-workgroup partial sums,
+ *            at least himuon_pair_stats_workspace(a, n) bytes, 8-byte aligned.
+ * stream   : hipStream_t to enqueue on.
+ * Products are exact in fp64 and summed in fp64 in a fixed order: the same
+ * inputs give the same bits on every run.
+ * Errors: HIMUON_ERR_INVALID_ARGUMENT (null pointer, size < 1, ld < cols,
+ * shapes that differ), HIMUON_ERR_UNSUPPORTED (dtype), HIMUON_ERR_LAYOUT
+ * (misaligned pointer), HIMUON_ERR_WORKSPACE (workspace NULL or too small),
+ * HIMUON_ERR_HIP (launch refused).  n == 0 is a no-op.
+ */
+himuon_status_t himuon_pair_stats(const himuon_matrix_t* a, const himuon_matrix_t* b, int32_t n,
+                                  himuon_dtype_t dt, double* out, void* workspace, size_t workspace_bytes,
+                                  void* stream);
+
+/* Bytes of workspace himuon_pair_stats needs for pairs of these shapes (the
+ * shapes of `a`; pointers are not read).  Host-side only. */
+himuon_status_t himuon_pair_stats_workspace(const himuon_matrix_t* a, int32_t n, size_t* bytes);
+
 /* Static description of a status code (never NULL). */
 const char* himuon_status_string(himuon_status_t s);
 

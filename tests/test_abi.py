@@ -266,3 +266,59 @@ def test_schedule_validation():
     assert f(d, 1, None, 3, abc, H.BF16, 1e-7, None, 0, None) == 1                # no sizes
     # a pass that needs a workspace (T = 512: step path) without one
     assert f(d, 1, ts(512, 256, 128), 3, abc, H.BF16, 1e-7, None, 0, None) == 5
+
+
+def test_pair_stats_workspace_and_validation():
+    """Pair statistics: workspace size from the shapes (one partial of three
+    doubles per band of about 64k elements), and every argument error found on
+    the host before any launch (placeholder pointers are never read)."""
+    P = ctypes.POINTER
+    shapes = [(2048, 5632), (5632, 2048), (1, 1), (3, 70000)]
+    a = (H.himuon_matrix_t * len(shapes))(*[sd(r, c) for r, c in shapes])
+    want = 0
+    for r, c in shapes:
+        R = max(1, min(-(-65536 // c), r))
+        want += -(-r // R)
+    assert H.himuon_pair_stats_workspace(a) == want * 24
+    assert H.himuon_pair_stats_workspace([]) == 0
+    nb = ctypes.c_size_t(0)
+    assert H.lib.himuon_pair_stats_workspace(a, len(shapes), None) == 1
+    assert H.lib.himuon_pair_stats_workspace(None, 1, ctypes.byref(nb)) == 1
+    bad = (H.himuon_matrix_t * 1)(sd(0, 5))
+    assert H.lib.himuon_pair_stats_workspace(bad, 1, ctypes.byref(nb)) == 1
+
+    ws, out = ctypes.c_void_p(1 << 24), ctypes.c_void_p(1 << 26)
+    big = 1 << 40
+
+    def call(x, y, n=1, dt=H.BF16, o=out, w=ws, wb=big):
+        return H.lib.himuon_pair_stats(x, y, n, dt, o, w, wb, None)
+
+    x = (H.himuon_matrix_t * 1)(sd(64, 96))
+    y = (H.himuon_matrix_t * 1)(sd(64, 96, ptr=1 << 22))
+    assert call(x, y, n=0) == 0                                   # no-op
+    assert call(x, y, dt=7) == 2                                  # dtype
+    assert call(x, y, n=-1) == 1
+    assert call(None, y) == 1 and call(x, None) == 1
+    assert call(x, y, o=None) == 1
+    assert call(x, (H.himuon_matrix_t * 1)(sd(64, 95, ptr=1 << 22))) == 1   # shapes differ
+    assert call(x, (H.himuon_matrix_t * 1)(sd(64, 96, ld=90, ptr=1 << 22))) == 1   # ld < cols
+    assert call(x, (H.himuon_matrix_t * 1)(sd(64, 96, ptr=(1 << 22) + 1))) == 3   # misaligned
+    assert call(x, y, o=ctypes.c_void_p((1 << 26) + 4)) == 3      # out not 8-byte aligned
+    assert call(x, y, w=None) == 5
+    need = H.himuon_pair_stats_workspace(x)
+    assert call(x, y, wb=need - 1) == 5
+    assert call(x, y, w=ctypes.c_void_p((1 << 24) + 4)) == 3
+
+
+def test_one_hip_runtime_after_import():
+    """Importing the binding first (as this file does, before any GPU test)
+    must leave one HIP runtime in the process: the library binds to torch's,
+    which owns the device memory and streams it is handed."""
+    import subprocess
+    import sys
+    code = ("import os, tiled_newton_schulz_amd, torch\n"
+            "m = open(f'/proc/{os.getpid()}/maps').read()\n"
+            "print(len({l.split()[-1] for l in m.splitlines() if 'libamdhip64' in l}))\n")
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT, timeout=300)
+    assert out.returncode == 0, out.stderr[-2000:]
+    assert out.stdout.strip() == "1"

@@ -21,7 +21,8 @@ MAX_STEPS = 16
 STATUS = {0: "HIMUON_OK", 1: "HIMUON_ERR_INVALID_ARGUMENT", 2: "HIMUON_ERR_UNSUPPORTED",
           3: "HIMUON_ERR_LAYOUT", 4: "HIMUON_ERR_OVERLAP", 5: "HIMUON_ERR_WORKSPACE", 6: "HIMUON_ERR_HIP"}
 EXPORTS = ["himuon_plan", "himuon_workspace_size", "himuon_tiled_ns", "himuon_tiled_ns_schedule",
-           "himuon_muon_step", "himuon_status_string", "himuon_last_hip_error", "himuon_version"]
+           "himuon_muon_step", "himuon_pair_stats", "himuon_pair_stats_workspace", "himuon_status_string",
+           "himuon_last_hip_error", "himuon_version"]
 
 
 class himuon_matrix_t(ctypes.Structure):
@@ -46,6 +47,12 @@ class HimuonError(RuntimeError):
 
 
 def _load():
+    # torch first: it brings its own HIP runtime (same soname as the system
+    # one), and the library must bind to that instance, the one that owns the
+    # device memory and streams it is handed.  Loaded the other way round, the
+    # process would hold two HIP runtimes and the library's would see no device.
+    import torch  # noqa: F401
+
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run `python tiled_newton_schulz_amd/build.py` "
                           "(or __graft_entry__.build()) first")
@@ -70,6 +77,11 @@ def _load():
                                    ctypes.c_float, ctypes.c_int, ctypes.c_float, ctypes.c_void_p,
                                    ctypes.c_size_t, ctypes.c_void_p]
     L.himuon_muon_step.restype = ctypes.c_int
+    L.himuon_pair_stats.argtypes = [P(himuon_matrix_t), P(himuon_matrix_t), ctypes.c_int32, ctypes.c_int,
+                                    ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    L.himuon_pair_stats.restype = ctypes.c_int
+    L.himuon_pair_stats_workspace.argtypes = [P(himuon_matrix_t), ctypes.c_int32, P(ctypes.c_size_t)]
+    L.himuon_pair_stats_workspace.restype = ctypes.c_int
     L.himuon_status_string.argtypes = [ctypes.c_int]
     L.himuon_status_string.restype = ctypes.c_char_p
     L.himuon_last_hip_error.argtypes = []
@@ -241,6 +253,49 @@ def himuon_muon_step(W: Sequence, M: Sequence, G: Sequence, T: int, K: int, abc=
                                 ctypes.c_void_p(ptr), nbytes, _stream_handle(stream))
     _check(code, "himuon_muon_step")
     return ws
+
+
+def himuon_pair_stats_workspace(a: Sequence) -> int:
+    """Workspace bytes himuon_pair_stats needs for pairs shaped like `a`."""
+    d = _descs(a)
+    nbytes = ctypes.c_size_t(0)
+    _check(lib.himuon_pair_stats_workspace(d, len(a), ctypes.byref(nbytes)), "himuon_pair_stats_workspace")
+    return nbytes.value
+
+
+def _row_major(t) -> bool:
+    return t.stride(1) == 1 or t.shape[1] == 1
+
+
+def himuon_pair_stats(a: Sequence, b: Sequence, out=None, workspace=None, stream=None):
+    """(n, 3) float64 device tensor: sum a*b, sum a*a, sum b*b for each pair.
+
+    a[i] and b[i] are equal-shaped bf16 or fp32 tensors with the same memory
+    orientation (both row-major, or both transposed views); `out` and
+    `workspace` are optional device tensors (float64 of 3n elements, uint8)."""
+    import torch
+    n = len(a)
+    if len(b) != n:
+        raise ValueError("a and b must have equal length")
+    if n == 0:
+        return torch.empty((0, 3), dtype=torch.float64)
+    dtype = _dtype_code(a[0])
+    for x, y in zip(a, b):
+        if x.shape != y.shape:
+            raise ValueError("pairs must have equal shapes")
+        if _row_major(x) != _row_major(y):
+            raise ValueError("both matrices of a pair must have the same orientation")
+    da, db = _descs(a), _descs(b)
+    dev = a[0].device
+    if out is None:
+        out = torch.empty((n, 3), dtype=torch.float64, device=dev)
+    if workspace is None:
+        workspace = torch.empty(max(himuon_pair_stats_workspace(a), 8), dtype=torch.uint8, device=dev)
+    nbytes = workspace.numel() * workspace.element_size()
+    code = lib.himuon_pair_stats(da, db, n, dtype, ctypes.c_void_p(out.data_ptr()),
+                                 ctypes.c_void_p(workspace.data_ptr()), nbytes, _stream_handle(stream))
+    _check(code, "himuon_pair_stats")
+    return out
 
 
 def himuon_status_string(code: int) -> str:

@@ -19,7 +19,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(HERE, "libhimuon.so")
 OBJDIR = os.path.join(ROOT, "_build")
-SOURCES = ["resident.hip", "resident256.hip", "stepwise.hip", "api.cpp"]
+SOURCES = ["resident.hip", "resident256.hip", "stepwise.hip", "pair_stats.hip", "api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -12,6 +12,7 @@
 #include <vector>
 
 #include "common.h"
+#include "pair_stats.h"
 
 using namespace himuon;
 
@@ -480,6 +481,29 @@ himuon_status_t run(const std::vector<MatSpec>& specs, int32_t T, int32_t K, con
     return HIMUON_OK;
 }
 
+// ---- pair statistics ----------------------------------------------------
+constexpr int64_t kPairBandElems = 65536;   // elements one workgroup reduces (about)
+
+int32_t pair_rows_per_block(int64_t rows, int64_t cols) {
+    const int64_t r = (kPairBandElems + cols - 1) / cols;
+    return (int32_t)std::max<int64_t>(1, std::min<int64_t>(r, rows));
+}
+
+// Workgroups (one partial each) over all pairs, from the shapes of `a`.
+himuon_status_t pair_blocks(const himuon_matrix_t* a, int32_t n, int64_t* total) {
+    if (n < 0 || (n > 0 && a == nullptr)) return HIMUON_ERR_INVALID_ARGUMENT;
+    int64_t t = 0;
+    for (int32_t i = 0; i < n; ++i) {
+        if (a[i].rows < 1 || a[i].cols < 1) return HIMUON_ERR_INVALID_ARGUMENT;
+        if (a[i].rows > INT32_MAX || a[i].cols > INT32_MAX) return HIMUON_ERR_LAYOUT;
+        const int32_t R = pair_rows_per_block(a[i].rows, a[i].cols);
+        t += (a[i].rows + R - 1) / R;
+    }
+    if (t > INT32_MAX) return HIMUON_ERR_LAYOUT;
+    *total = t;
+    return HIMUON_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -588,6 +612,69 @@ himuon_status_t himuon_muon_step(const himuon_matrix_t* W, const himuon_matrix_t
     return run(specs, T, K, abc, dt, eps, mu, eta, true, workspace, workspace_bytes, stream);
 }
 
+himuon_status_t himuon_pair_stats_workspace(const himuon_matrix_t* a, int32_t n, size_t* bytes) {
+    if (bytes == nullptr) return HIMUON_ERR_INVALID_ARGUMENT;
+    int64_t total = 0;
+    himuon_status_t st = pair_blocks(a, n, &total);
+    if (st != HIMUON_OK) return st;
+    *bytes = (size_t)total * 3 * sizeof(double);
+    return HIMUON_OK;
+}
+
+himuon_status_t himuon_pair_stats(const himuon_matrix_t* a, const himuon_matrix_t* b, int32_t n, himuon_dtype_t dt,
+                                  double* out, void* workspace, size_t workspace_bytes, void* stream) {
+    if (dt != HIMUON_BF16 && dt != HIMUON_FP32) return HIMUON_ERR_UNSUPPORTED;
+    if (n < 0) return HIMUON_ERR_INVALID_ARGUMENT;
+    if (n == 0) return HIMUON_OK;
+    if (a == nullptr || b == nullptr || out == nullptr) return HIMUON_ERR_INVALID_ARGUMENT;
+    if ((reinterpret_cast<uintptr_t>(out) % sizeof(double)) != 0) return HIMUON_ERR_LAYOUT;
+    const size_t es = elem_size(dt);
+    for (int32_t i = 0; i < n; ++i) {
+        himuon_status_t st = check_matrix(a[i], es);
+        if (st != HIMUON_OK) return st;
+        if ((st = check_matrix(b[i], es)) != HIMUON_OK) return st;
+        if (a[i].rows != b[i].rows || a[i].cols != b[i].cols) return HIMUON_ERR_INVALID_ARGUMENT;
+    }
+    int64_t total = 0;
+    himuon_status_t st = pair_blocks(a, n, &total);
+    if (st != HIMUON_OK) return st;
+    const size_t need = (size_t)total * 3 * sizeof(double);
+    if (workspace == nullptr || workspace_bytes < need) return HIMUON_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) % sizeof(double)) != 0) return HIMUON_ERR_LAYOUT;
+
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    int32_t part = 0;
+    for (int32_t g0 = 0; g0 < n; g0 += kPairGroup) {
+        PairArgs pa{};
+        pa.n = std::min<int32_t>(kPairGroup, n - g0);
+        pa.dtype = dt == HIMUON_BF16 ? 0 : 1;
+        pa.partial = reinterpret_cast<double*>(workspace);
+        pa.out = out + 3 * (int64_t)g0;
+        int32_t blocks = 0;
+        for (int32_t k = 0; k < pa.n; ++k) {
+            const himuon_matrix_t& x = a[g0 + k];
+            const himuon_matrix_t& y = b[g0 + k];
+            PairEntry& e = pa.e[k];
+            e.a = x.ptr;
+            e.b = y.ptr;
+            e.lda = x.ld;
+            e.ldb = y.ld;
+            e.rows = (int32_t)x.rows;
+            e.cols = (int32_t)x.cols;
+            e.rows_per_block = pair_rows_per_block(x.rows, x.cols);
+            e.nblocks = (int32_t)((x.rows + e.rows_per_block - 1) / e.rows_per_block);
+            e.block_base = blocks;
+            e.part_base = part;
+            blocks += e.nblocks;
+            part += e.nblocks;
+        }
+        pa.total_blocks = blocks;
+        hipError_t e = launch_pair_stats(pa, s);
+        if (e != hipSuccess) return hip_fail(e);
+    }
+    return HIMUON_OK;
+}
+
 const char* himuon_status_string(himuon_status_t s) {
     switch (s) {
         case HIMUON_OK: return "ok";
@@ -603,6 +690,6 @@ const char* himuon_status_string(himuon_status_t s) {
 
 int32_t himuon_last_hip_error(void) { return g_last_hip; }
 
-int32_t himuon_version(void) { return 10100; }
+int32_t himuon_version(void) { return 10200; }
 
 }  // extern "C"
