@@ -34,10 +34,14 @@ __device__ __forceinline__ float lo_f(unsigned u) { return __uint_as_float(u << 
 __device__ __forceinline__ float hi_f(unsigned u) { return __uint_as_float(u & 0xffff0000u); }
 
 // Registers off..off+7 of an accumulator block as one bf16 MFMA operand.
+// The packed words are made opaque to the optimiser: otherwise it rewrites a
+// later lo_f(word) (a shift of the word) as a fresh one-element conversion
+// plus a shift, one extra VALU instruction per unpacked element.
 __device__ __forceinline__ u32x4 cvt8(const f32x16& v, int off) {
     u32x4 r;
 #pragma unroll
     for (int k = 0; k < 4; ++k) r[k] = pack2(v[off + 2 * k], v[off + 2 * k + 1]);
+    asm("" : "+v"(r));
     return r;
 }
 // The bf16 rounding error of those registers, itself rounded to bf16.
@@ -51,6 +55,13 @@ __device__ __forceinline__ u32x4 cvt8_lo(const f32x16& v, int off, u32x4 hi) {
 __device__ __forceinline__ f32x16 mfma32w(u32x4 a, u32x4 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
                                                    c, 0, 0, 0);
+}
+
+// a_t on the diagonal of a diagonal AL block: element q of lane (l32, g) sits
+// at row (q/4) 8 + 4 g + q%4 and column l32.  B' = a I + b A + c A^2 is formed
+// as fma(c, A^2, fma(b, A, this)), so the identity costs no extra instruction.
+__device__ __forceinline__ float diag_term(int q, int l32, int g, float ca) {
+    return ((q >> 2) * 8 + g * 4 + (q & 3) == l32) ? ca : 0.f;
 }
 
 __device__ __forceinline__ float wave_sum(float v) {

@@ -307,8 +307,8 @@ __global__ __launch_bounds__(64) void resident_kernel(const ResidentArgs args) {
         // B = b A + c A^2 (A symmetric: AL(A(K,P)) is the row operand of A(P,K))
         if constexpr (SYM) {
             // lower blocks (P >= Q), two chains at a time; a X is folded into
-            // the product: B' = a I + B (a added after the fma, so that c = 0
-            // is handled too).  Software pipelined: the
+            // the product: B' = a I + B, the identity entering through the
+            // linear term (c = 0 is handled too).  Software pipelined: the
             // products of the next pair are issued before this pair's epilogue
             // (VALU) and transposes, so the two overlap.
             constexpr int NL = NB * (NB + 1) / 2;
@@ -346,24 +346,22 @@ __global__ __launch_bounds__(64) void resident_kernel(const ResidentArgs args) {
                 const bool two = 2 * p + 1 < NL;
                 f32x16 a1 = c1, a2 = c2;
                 if (p + 1 < NP) products(p + 1, c1, c2);
+                // linear term b A (+ a on the diagonal of a diagonal block)
+                auto lin = [&](bool dg, int e, float av) {
+                    return dg ? __builtin_fmaf(cb, av, diag_term(e, l32, g, ca)) : cb * av;
+                };
 #pragma unroll
                 for (int f = 0; f < 2; ++f)
 #pragma unroll
                     for (int k = 0; k < 4; ++k) {
                         const int e = 8 * f + 2 * k;
-                        a1[e] = __builtin_fmaf(cc, a1[e], cb * lo_f(Abf[P1][Q1][f][k]));
-                        a1[e + 1] = __builtin_fmaf(cc, a1[e + 1], cb * hi_f(Abf[P1][Q1][f][k]));
+                        a1[e] = __builtin_fmaf(cc, a1[e], lin(P1 == Q1, e, lo_f(Abf[P1][Q1][f][k])));
+                        a1[e + 1] = __builtin_fmaf(cc, a1[e + 1], lin(P1 == Q1, e + 1, hi_f(Abf[P1][Q1][f][k])));
                         if (two) {
-                            a2[e] = __builtin_fmaf(cc, a2[e], cb * lo_f(Abf[P2][Q2][f][k]));
-                            a2[e + 1] = __builtin_fmaf(cc, a2[e + 1], cb * hi_f(Abf[P2][Q2][f][k]));
+                            a2[e] = __builtin_fmaf(cc, a2[e], lin(P2 == Q2, e, lo_f(Abf[P2][Q2][f][k])));
+                            a2[e + 1] = __builtin_fmaf(cc, a2[e + 1], lin(P2 == Q2, e + 1, hi_f(Abf[P2][Q2][f][k])));
                         }
                     }
-#pragma unroll
-                for (int q = 0; q < 16; ++q) {
-                    const bool diag = (q >> 2) * 8 + g * 4 + (q & 3) == l32;
-                    if (P1 == Q1 && diag) a1[q] += ca;
-                    if (two && P2 == Q2 && diag) a2[q] += ca;
-                }
                 Bbf[P1][Q1][0] = cvt8(a1, 0); Bbf[P1][Q1][1] = cvt8(a1, 8);
                 if (two) { Bbf[P2][Q2][0] = cvt8(a2, 0); Bbf[P2][Q2][1] = cvt8(a2, 8); }
                 if (P1 != Q1) transpose_al(0, Bbf[P1][Q1], Bbf[Q1][P1]);
@@ -677,19 +675,18 @@ __global__ __launch_bounds__(512) void resident_coop_kernel(const ResidentArgs a
                 }
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
+                const bool dg = 2 * h + i == c;
 #pragma unroll
                 for (int f = 0; f < 2; ++f)
 #pragma unroll
                     for (int k = 0; k < 4; ++k) {
                         const int e = 8 * f + 2 * k;
-                        acc[i][e] = __builtin_fmaf(cc, acc[i][e], cb * lo_f(Aown[i][f][k]));
-                        acc[i][e + 1] = __builtin_fmaf(cc, acc[i][e + 1], cb * hi_f(Aown[i][f][k]));
+                        const float l0 = lo_f(Aown[i][f][k]), l1 = hi_f(Aown[i][f][k]);
+                        acc[i][e] = __builtin_fmaf(cc, acc[i][e], dg ? __builtin_fmaf(cb, l0, diag_term(e, l32, g, ca))
+                                                                     : cb * l0);
+                        acc[i][e + 1] = __builtin_fmaf(
+                            cc, acc[i][e + 1], dg ? __builtin_fmaf(cb, l1, diag_term(e + 1, l32, g, ca)) : cb * l1);
                     }
-                if (2 * h + i == c) {
-#pragma unroll
-                    for (int q = 0; q < 16; ++q)
-                        if ((q >> 2) * 8 + g * 4 + (q & 3) == l32) acc[i][q] += ca;
-                }
                 Bown[i][0] = cvt8(acc[i], 0);
                 Bown[i][1] = cvt8(acc[i], 8);
             }

@@ -152,19 +152,18 @@ __device__ __forceinline__ void combine(f32x16 (&acc)[5], u32x4 (&p)[5][2], floa
     using B = Blocks<NR>;
 #pragma unroll
     for (int b = 0; b < B::n[W]; ++b) {
+        const bool dg = B::i[W][b] == B::j[W][b];
 #pragma unroll
         for (int f = 0; f < 2; ++f)
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 const int e = 8 * f + 2 * k;
-                acc[b][e] = __builtin_fmaf(cc, acc[b][e], cb * lo_f(p[b][f][k]));
-                acc[b][e + 1] = __builtin_fmaf(cc, acc[b][e + 1], cb * hi_f(p[b][f][k]));
+                const float l0 = lo_f(p[b][f][k]), l1 = hi_f(p[b][f][k]);
+                // linear term b A, with a on the diagonal of a diagonal block
+                acc[b][e] = __builtin_fmaf(cc, acc[b][e], dg ? __builtin_fmaf(cb, l0, diag_term(e, l32, g, ca)) : cb * l0);
+                acc[b][e + 1] =
+                    __builtin_fmaf(cc, acc[b][e + 1], dg ? __builtin_fmaf(cb, l1, diag_term(e + 1, l32, g, ca)) : cb * l1);
             }
-        if (B::i[W][b] == B::j[W][b]) {
-#pragma unroll
-            for (int q = 0; q < 16; ++q)
-                if ((q >> 2) * 8 + g * 4 + (q & 3) == l32) acc[b][q] += ca;
-        }
         p[b][0] = cvt8(acc[b], 0);
         p[b][1] = cvt8(acc[b], 8);
     }
