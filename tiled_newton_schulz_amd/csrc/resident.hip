@@ -419,17 +419,26 @@ __global__ __launch_bounds__(64) void resident_kernel(const ResidentArgs args) {
         // (B' of the last block pair is an input, so the hook stays after B')
         before_apply(Bbf[NB - 1][NB - 1][1][3]);
         // X' = a X + B X, computed as X'^T blocks so the result lands in RL
-#pragma unroll
-        for (int J = 0; J < NB; ++J) {
-            u32x4 opA[NB][2];
-            u32x4 opL[SPLIT_X ? NB : 1][2];
+        // The operands of column block J + 1 are read before the results of
+        // block J are written back (those go to column block J): the reads are
+        // then in flight during block J's products instead of waiting behind
+        // its stores, which the compiler cannot reorder them across.
+        u32x4 opA[2][NB][2];
+        u32x4 opL[2][SPLIT_X ? NB : 1][2];
+        auto load_ops = [&](int J, int buf) __attribute__((always_inline)) {
 #pragma unroll
             for (int K = 0; K < NB; ++K)
 #pragma unroll
                 for (int f = 0; f < 2; ++f) {
-                    opA[K][f] = tr_frag(sX, K, J, f);
-                    if constexpr (SPLIT_X) opL[K][f] = tr_frag(sXl, K, J, f);
+                    opA[buf][K][f] = tr_frag(sX, K, J, f);
+                    if constexpr (SPLIT_X) opL[buf][K][f] = tr_frag(sXl, K, J, f);
                 }
+        };
+        load_ops(0, 0);
+#pragma unroll
+        for (int J = 0; J < NB; ++J) {
+            const int cur = J & 1;
+            if (J + 1 < NB) load_ops(J + 1, cur ^ 1);
             f32x16 acc[NB];
 #pragma unroll
             for (int I = 0; I < NB; ++I) {
@@ -442,9 +451,9 @@ __global__ __launch_bounds__(64) void resident_kernel(const ResidentArgs args) {
                 for (int f = 0; f < 2; ++f)
 #pragma unroll
                     for (int I = 0; I < NB; ++I) {
-                        acc[I] = mfma32w(opA[K][f], Bbf[K][I][f], acc[I]);
-                        if constexpr (SPLIT_B) acc[I] = mfma32w(opA[K][f], Blo[K][I][f], acc[I]);
-                        if constexpr (SPLIT_X) acc[I] = mfma32w(opL[K][f], Bbf[K][I][f], acc[I]);
+                        acc[I] = mfma32w(opA[cur][K][f], Bbf[K][I][f], acc[I]);
+                        if constexpr (SPLIT_B) acc[I] = mfma32w(opA[cur][K][f], Blo[K][I][f], acc[I]);
+                        if constexpr (SPLIT_X) acc[I] = mfma32w(opL[cur][K][f], Bbf[K][I][f], acc[I]);
                     }
 #pragma unroll
             for (int I = 0; I < NB; ++I) {
