@@ -51,7 +51,8 @@
 namespace himuon {
 
 template <int TK, bool MUON, bool PRECISE>
-__global__ __launch_bounds__(64) void resident_kernel(const ResidentArgs args) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(TK == 64 && !PRECISE ? 4 : 1)))
+void resident_kernel(const ResidentArgs args) {
     constexpr int NB = TK / 32;          // 32x32 blocks per side
     constexpr int LD = TK + 8;           // LDS row stride (elements), 16-byte pad
     // fp32 copy of the tile in registers for kernel tile 32 and the split
@@ -80,7 +81,10 @@ __global__ __launch_bounds__(64) void resident_kernel(const ResidentArgs args) {
     // back with ds_read_tr16_b64.
     constexpr bool SYM = !MASTER32;
     constexpr int LDT = 40;   // staging row stride (elements)
-    __shared__ __attribute__((aligned(16))) unsigned short sT[SYM ? 2 * 32 * LDT : 8];
+    // Kernel tile 64 has one off-diagonal lower block, so one staging slot;
+    // a smaller LDS footprint lets 13 rather than 11 tiles share a CU.
+    constexpr int NSLOT = TK == 64 ? 1 : 2;
+    __shared__ __attribute__((aligned(16))) unsigned short sT[SYM ? NSLOT * 32 * LDT : 8];
 
     u16x8 chunk[IO::NCH];   // the tile as loaded: bf16 16-byte chunks, row-major order
     bool loaded = false;    // chunk already holds tile t (loaded during the tile before)
@@ -157,7 +161,7 @@ __global__ __launch_bounds__(64) void resident_kernel(const ResidentArgs args) {
     // as its transpose, row-major (lane l writes row l%32), then read the AL of
     // the stored matrix, which is AL of the transpose.
     auto transpose_al = [&](int slot, const u32x4 (&in)[2], u32x4 (&out)[2]) {
-        unsigned short* buf = &sT[slot * 32 * LDT];
+        unsigned short* buf = &sT[(NSLOT == 1 ? 0 : slot) * 32 * LDT];
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             u32x2 v = {in[m >> 1][2 * (m & 1)], in[m >> 1][2 * (m & 1) + 1]};
