@@ -356,6 +356,36 @@ def test_dense8192_cap(cuda, T):
             assert torch.equal(a, b)
 
 
+def test_full_map_operand_past_2gib(cuda):
+    """The full-matrix map of a 16384 x 65536 bf16 matrix: its oriented operand
+    is 2 GiB, past the 32-bit buffer offsets of the DMA GEMM, so the step path
+    runs its register-staged GEMM with 64-bit addressing.  A rank-one input
+    u v^T with +-1 entries has a closed-form result (SVD view of the iteration,
+    Gram Newton-Schulz page, section 3): its one singular value, normalised to
+    ||Y||_F / (||Y||_F + eps), goes through the step polynomial, so every output
+    element is +-p(s) / ||Y||_F with the input's sign.  Random signs make any
+    misplaced element show."""
+    from oracle import diagnostics as OD
+    Hh, Ww = 16384, 65536
+    g = torch.Generator(device="cpu").manual_seed(61)
+    u = (torch.randint(0, 2, (Hh,), generator=g) * 2 - 1).to(torch.float32).to(cuda)
+    v = (torch.randint(0, 2, (Ww,), generator=g) * 2 - 1).to(torch.float32).to(cuda)
+    m = torch.outer(u, v).to(torch.bfloat16)
+    plan = H.himuon_plan([m], max(Hh, Ww), 5, H.BF16, 16 << 30)
+    assert plan["chunks"] == 1 and plan["resident_launches"] == 0
+    say(f"full map of {Hh}x{Ww} bf16 (operand {Hh * Ww * 2 / 2**30:.1f} GiB)")
+    run([m], max(Hh, Ww))
+    norm = math.sqrt(Hh * Ww)
+    s = float(OD.scalar_map(norm / (norm + oracle.EPS_DEFAULT), [COEFFS] * 5))
+    got = m.float() * (norm / s)            # should be the +-1 pattern
+    want = torch.outer(u, v)
+    rel = (got - want).abs().max().item()
+    say(f"  p(s) = {s:.6f}, worst element relative error {rel:.3e}")
+    assert rel <= 3e-2
+    del got, want, m
+    torch.cuda.empty_cache()
+
+
 def test_tail_split_bit_exact(cuda):
     """The partial last round of kernel-tile-128 tiles runs eight waves per tile;
     its arithmetic is the one-wave kernel's, so a batched call (3,072 tiles
