@@ -175,6 +175,47 @@ himuon_status_t himuon_muon_step(const himuon_matrix_t* W, const himuon_matrix_t
                                  float eps, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * himuon_gram_ns - the full-matrix Newton-Schulz map of each matrix, in place,
+ * computed through its Gram matrix ("Gram Newton-Schulz" summary page,
+ * section 6, Algorithm 3, stabilised Gram Newton-Schulz with a restart).
+ *
+ * Each matrix Y is normalised, X = Y / (||Y||_F + eps), and oriented so that
+ * X is r x s with r <= s (a tall matrix is worked on transposed).  The steps
+ * then run on r x r matrices:
+ *     R = X X^T,  Q = I;   for t = 1..K:
+ *         P = a_t I + b_t R + c_t R^2,   Q <- P Q,   R <- P R P
+ * and the result Q X is written back (in the matrix's own orientation).  In
+ * exact arithmetic this equals himuon_tiled_ns with T >= max(rows, cols); the
+ * iteration costs about 4 r^3 flops a step instead of 4 r^2 s + 2 r^3, so it
+ * pays for wide matrices (s well above r).  Before step restart + 1 the
+ * iteration restarts (the page restarts before its third step, restart = 2):
+ * X <- Q X,  R <- X X^T,  Q <- I, which removes the rounding R has gathered.
+ *
+ * m, n       : n >= 0 matrix descriptors, as for himuon_tiled_ns.
+ * K, abc     : steps and coefficients, as for himuon_tiled_ns.
+ * restart    : >= 0; 0 (or >= K) never restarts (the page's Algorithm 2).
+ * dt, eps    : as for himuon_tiled_ns.
+ * workspace, workspace_bytes : device scratch, at least the *min of
+ *              himuon_gram_ns_workspace; matrices are processed in chunks
+ *              that fit (every matrix runs on the step-by-step path; K = 0
+ *              writes the normalised matrices as himuon_tiled_ns does).
+ * stream     : hipStream_t to enqueue on.
+ * The workspace holds the iterates in bf16 when dt is bf16 and both sides of
+ * the matrix are at least 32, else in fp32.
+ * Errors: HIMUON_ERR_INVALID_ARGUMENT for restart < 0, otherwise as for
+ * himuon_tiled_ns (HIMUON_ERR_LAYOUT also for a side above INT32_MAX).
+ */
+himuon_status_t himuon_gram_ns(const himuon_matrix_t* m, int32_t n, int32_t K, const float* abc,
+                               int32_t restart, himuon_dtype_t dt, float eps, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace himuon_gram_ns needs for these matrices in one chunk
+ * (*full) and for its largest single matrix (*min).  Host-side only; either
+ * output pointer may be NULL. */
+himuon_status_t himuon_gram_ns_workspace(const himuon_matrix_t* m, int32_t n, himuon_dtype_t dt,
+                                         size_t* full, size_t* min);
+
+/*
  * himuon_pair_stats - for n pairs of equal-shaped matrices (a[i], b[i]) the
  * three sums  sum a*b,  sum a*a,  sum b*b  over all elements, in fp64.
  *

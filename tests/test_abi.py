@@ -322,3 +322,37 @@ def test_one_hip_runtime_after_import():
     out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT, timeout=300)
     assert out.returncode == 0, out.stderr[-2000:]
     assert out.stdout.strip() == "1"
+
+
+def test_gram_ns_workspace_and_validation():
+    """himuon_gram_ns: every matrix is one tile on the step path with two
+    oriented X areas and four r x r areas (R, the step polynomial, the running
+    product, a spare) plus the norm partials; bf16 keeps a bf16 workspace when
+    both sides are >= 32, else fp32.  Errors come before any launch."""
+    al = lambda x: (x + 255) // 256 * 256
+    r8 = lambda x: (x + 7) // 8 * 8
+    for h, w, dt in [(2048, 5632, H.BF16), (5632, 2048, H.BF16), (300, 170, H.FP32), (20, 700, H.BF16),
+                     (64, 64, H.BF16)]:
+        r, s_ = min(h, w), max(h, w)
+        es = 4 if dt == H.FP32 or r < 32 else 2
+        want = 2 * al(es * r * r8(s_)) + 4 * al(es * r * r8(r)) + al(32 * 4)
+        assert H.himuon_gram_ns_workspace([sd(h, w)], dt) == (want, want), (h, w)
+    # several matrices: one chunk holds them all; min is the largest single one
+    full, mn = H.himuon_gram_ns_workspace([sd(1024, 4096), sd(512, 512, ptr=1 << 34)], H.BF16)
+    one = lambda r, s_: 2 * al(2 * r * s_) + 4 * al(2 * r * r) + al(32 * 4)
+    assert mn == one(1024, 4096)
+    assert full == 2 * al(2 * (1024 * 4096 + 512 * 512)) + 4 * al(2 * (1024 * 1024 + 512 * 512)) + al(2 * 32 * 4)
+
+    def call(descs, K=5, restart=2, ws=None, nbytes=0, dt=H.BF16):
+        arr = (H.himuon_matrix_t * max(1, len(descs)))(*descs)
+        abc = H.coeff_array((3.4445, -4.775, 2.0315), K)
+        return H.lib.himuon_gram_ns(arr, len(descs), K, abc, restart, dt, 1e-7, ws, nbytes, None)
+
+    assert call([]) == 0
+    assert call([sd(256, 512)], restart=-1) == 1
+    assert call([H.himuon_matrix_t(None, 64, 64, 64)]) == 1
+    assert call([sd(256, 512)], K=17) == 1
+    assert call([sd(256, 512)]) == 5                                         # no workspace
+    assert call([sd(256, 512)], ws=ctypes.c_void_p(1 << 30), nbytes=1000) == 5
+    assert call([sd(1, (1 << 31) + 8)]) == 3                                 # side past the int32 grid
+    assert call([H.himuon_matrix_t((1 << 20) + 1, 64, 64, 64)]) == 3

@@ -21,7 +21,8 @@ MAX_STEPS = 16
 STATUS = {0: "HIMUON_OK", 1: "HIMUON_ERR_INVALID_ARGUMENT", 2: "HIMUON_ERR_UNSUPPORTED",
           3: "HIMUON_ERR_LAYOUT", 4: "HIMUON_ERR_OVERLAP", 5: "HIMUON_ERR_WORKSPACE", 6: "HIMUON_ERR_HIP"}
 EXPORTS = ["himuon_plan", "himuon_workspace_size", "himuon_tiled_ns", "himuon_tiled_ns_schedule",
-           "himuon_muon_step", "himuon_pair_stats", "himuon_pair_stats_workspace", "himuon_status_string",
+           "himuon_muon_step", "himuon_gram_ns", "himuon_gram_ns_workspace", "himuon_pair_stats",
+           "himuon_pair_stats_workspace", "himuon_status_string",
            "himuon_last_hip_error", "himuon_version"]
 
 
@@ -77,6 +78,13 @@ def _load():
                                    ctypes.c_float, ctypes.c_int, ctypes.c_float, ctypes.c_void_p,
                                    ctypes.c_size_t, ctypes.c_void_p]
     L.himuon_muon_step.restype = ctypes.c_int
+    L.himuon_gram_ns.argtypes = [P(himuon_matrix_t), ctypes.c_int32, ctypes.c_int32, P(ctypes.c_float),
+                                 ctypes.c_int32, ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t,
+                                 ctypes.c_void_p]
+    L.himuon_gram_ns.restype = ctypes.c_int
+    L.himuon_gram_ns_workspace.argtypes = [P(himuon_matrix_t), ctypes.c_int32, ctypes.c_int,
+                                           P(ctypes.c_size_t), P(ctypes.c_size_t)]
+    L.himuon_gram_ns_workspace.restype = ctypes.c_int
     L.himuon_pair_stats.argtypes = [P(himuon_matrix_t), P(himuon_matrix_t), ctypes.c_int32, ctypes.c_int,
                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     L.himuon_pair_stats.restype = ctypes.c_int
@@ -253,6 +261,41 @@ def himuon_muon_step(W: Sequence, M: Sequence, G: Sequence, T: int, K: int, abc=
                                 ctypes.c_void_p(ptr), nbytes, _stream_handle(stream))
     _check(code, "himuon_muon_step")
     return ws
+
+
+def himuon_gram_ns_workspace(mats: Sequence, dtype: int | None = None) -> tuple[int, int]:
+    """(full, min) workspace bytes of himuon_gram_ns for these matrices."""
+    if dtype is None:
+        dtype = _dtype_code(mats[0])
+    d = _descs(mats)
+    full, mn = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    _check(lib.himuon_gram_ns_workspace(d, len(mats), dtype, ctypes.byref(full), ctypes.byref(mn)),
+           "himuon_gram_ns_workspace")
+    return full.value, mn.value
+
+
+def himuon_gram_ns(mats: Sequence, K: int, abc=(3.4445, -4.7750, 2.0315), restart: int = 2, eps: float = 1e-7,
+                   workspace=None, workspace_bytes: int | None = None, stream=None):
+    """Full-matrix Newton-Schulz of each matrix, in place, through its Gram
+    matrix with a restart before step restart + 1 (0: none)."""
+    if len(mats) == 0:
+        return
+    dtype = _dtype_code(mats[0])
+    d = _descs(mats)
+    if workspace is None:
+        full = himuon_gram_ns_workspace(mats, dtype)[0]
+        cap = full if workspace_bytes is None else max(min(full, workspace_bytes), 0)
+        if cap:
+            import torch
+            workspace = torch.empty(cap, dtype=torch.uint8, device=mats[0].device)
+        workspace_bytes = cap
+    elif workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    ptr = workspace.data_ptr() if workspace is not None else None
+    code = lib.himuon_gram_ns(d, len(mats), K, coeff_array(abc, K), restart, dtype, eps,
+                              ctypes.c_void_p(ptr), workspace_bytes, _stream_handle(stream))
+    _check(code, "himuon_gram_ns")
+    return workspace
 
 
 def himuon_pair_stats_workspace(a: Sequence) -> int:

@@ -178,8 +178,33 @@ struct Plan {
     int64_t launches = 0;
 };
 
-size_t chunk_bytes(int64_t xel, int64_t ael, int64_t tiles, size_t es) {
-    return align_up((size_t)xel * es) * 2 + align_up((size_t)ael * es) * 2 + align_up((size_t)tiles * kWgNormMax * 4);
+// Workspace of one chunk: the current and next oriented tiles, `sq` areas of
+// r x r matrices (the standard step keeps A and B'; the Gram iteration keeps
+// R, its step polynomial, the running product and a spare) and the norm
+// partials.
+size_t chunk_bytes(int64_t xel, int64_t ael, int64_t tiles, size_t es, int sq) {
+    return align_up((size_t)xel * es) * 2 + align_up((size_t)ael * es) * sq + align_up((size_t)tiles * kWgNormMax * 4);
+}
+
+// Kernel launches of the Gram iteration for one chunk: two norm passes,
+// R = X X^T, per step the polynomial, the running product (not on the first
+// step after a start or restart, where it is the polynomial itself) and the
+// two products of the R update (not after the last step, nor before a
+// restart, which rebuilds R); a restart applies Q and rebuilds R; at the end
+// Q is applied once.
+int64_t gram_launches(int32_t K, int32_t restart) {
+    int64_t n = 4;
+    bool ident = true;
+    for (int32_t t = 1; t <= K; ++t) {
+        if (restart > 0 && t == restart + 1) {
+            n += 2;
+            ident = true;
+        }
+        n += ident ? 1 : 2;
+        ident = false;
+        if (t < K && !(restart > 0 && t == restart)) n += 2;
+    }
+    return n;
 }
 
 void oriented(const TileClass& c, int32_t& r, int32_t& sd) {
@@ -188,9 +213,12 @@ void oriented(const TileClass& c, int32_t& r, int32_t& sd) {
 }
 
 // Builds the plan.  With enforce_cap, every chunk's workspace stays within
-// `cap` (HIMUON_ERR_WORKSPACE if one tile alone does not fit).
+// `cap` (HIMUON_ERR_WORKSPACE if one tile alone does not fit).  gram: every
+// tile runs the Gram iteration on the step path (restart as for
+// himuon_gram_ns); bf16 tiles with both sides >= 32 keep a bf16 workspace,
+// the others fp32.
 himuon_status_t build_plan(const std::vector<MatSpec>& specs, int32_t T, int32_t K, himuon_dtype_t dt,
-                           size_t cap, bool enforce_cap, Plan& plan) {
+                           size_t cap, bool enforce_cap, Plan& plan, bool gram = false, int32_t restart = 0) {
     plan = Plan();
     std::vector<TileClass> all;
     for (size_t i = 0; i < specs.size(); ++i) {
@@ -198,8 +226,16 @@ himuon_status_t build_plan(const std::vector<MatSpec>& specs, int32_t T, int32_t
         classes_of(specs[i], (int)i, T, all);
     }
 
+    // step path workspace dtype of a class: 0 bf16, 1 fp32, -1 on chip
+    auto step_wk = [&](const TileClass& c) {
+        if (gram) return (dt == HIMUON_FP32 || std::min(c.th, c.tw) < 32) ? 1 : 0;
+        const Route r = route_of(dt, c.th, c.tw);
+        return r == Route::StepBf16 ? 0 : r == Route::StepFp32 ? 1 : -1;
+    };
+    const int sq = gram ? 4 : 2;
+
     // on-chip launches, keyed by (kernel tile, precision)
-    for (int precise = 0; precise < 2; ++precise)
+    for (int precise = 0; precise < (gram ? 0 : 2); ++precise)
         for (int kt : {32, 64, 128, 256})
           for (int narrow = 0; narrow < (kt == 256 ? 2 : 1); ++narrow) {
             Group cur;
@@ -232,8 +268,7 @@ himuon_status_t build_plan(const std::vector<MatSpec>& specs, int32_t T, int32_t
         cur.wk = wk;
         int64_t xo = 0, ao = 0;
         for (const TileClass& c : all) {
-            const Route r = route_of(dt, c.th, c.tw);
-            if (!((wk == 0 && r == Route::StepBf16) || (wk == 1 && r == Route::StepFp32))) continue;
+            if (step_wk(c) != wk) continue;
             if ((int)cur.cls.size() == kGroup || cur.tiles + c.tiles() > INT32_MAX / 64) {
                 plan.sgroups.push_back(cur);
                 cur = Group();
@@ -263,11 +298,11 @@ himuon_status_t build_plan(const std::vector<MatSpec>& specs, int32_t T, int32_t
             oriented(c, rr, ss);
             const int64_t xe = (int64_t)rr * round8(ss), ae = (int64_t)rr * round8(rr);
             const int32_t sb = ((c.th + 63) / 64) * ((c.tw + 63) / 64);
-            const size_t one = chunk_bytes(xe, ae, 1, es);
+            const size_t one = chunk_bytes(xe, ae, 1, es, sq);
             plan.ws_min = std::max(plan.ws_min, one);
             for (int64_t lt = 0; lt < c.tiles(); ++lt) {
                 const int32_t t = (int32_t)(G.tile_base[k] + lt);
-                if (open && enforce_cap && chunk_bytes(ch.xel + xe, ch.ael + ae, t + 1 - ch.tb, es) > cap) {
+                if (open && enforce_cap && chunk_bytes(ch.xel + xe, ch.ael + ae, t + 1 - ch.tb, es, sq) > cap) {
                     plan.chunks.push_back(ch);
                     open = false;
                 }
@@ -292,8 +327,8 @@ himuon_status_t build_plan(const std::vector<MatSpec>& specs, int32_t T, int32_t
     }
     for (const auto& c : plan.chunks) {
         const size_t es = plan.sgroups[c.group].wk == 0 ? 2 : 4;
-        plan.ws_full = std::max(plan.ws_full, chunk_bytes(c.xel, c.ael, c.te - c.tb, es));
-        plan.launches += 2 + 3LL * K;
+        plan.ws_full = std::max(plan.ws_full, chunk_bytes(c.xel, c.ael, c.te - c.tb, es, sq));
+        plan.launches += gram ? gram_launches(K, restart) : 2 + 3LL * K;
     }
     return HIMUON_OK;
 }
@@ -394,6 +429,42 @@ himuon_status_t hip_fail(hipError_t e) {
     return HIMUON_ERR_HIP;
 }
 
+// Step path arguments of one chunk, with its workspace laid out as
+// [X current | X next | nsq r x r areas | norm partials]; sq receives the r x r
+// area bases.
+void chunk_args(const std::vector<MatSpec>& specs, const Plan& plan, const Chunk& c, int32_t T, int32_t K,
+                const float* abc, himuon_dtype_t dt, float eps, float mu, float eta, bool muon, bool normalize,
+                void* ws, int nsq, StepArgs& a, char** sq) {
+    const Group& G = plan.sgroups[c.group];
+    const size_t es = G.wk == 0 ? 2 : 4;
+    a.nmats = (int32_t)G.cls.size();
+    for (size_t k = 0; k < G.cls.size(); ++k)
+        a.mats[k] = entry_of(specs[G.cls[k].spec], G.cls[k], G.tile_base[k], G.xoff[k], G.aoff[k]);
+    for (int i = 0; i < 3 * K; ++i) a.abc[i] = abc[i];
+    a.T = T;
+    a.K = K;
+    a.tile_begin = c.tb;
+    a.tile_end = c.te;
+    a.xbase = c.xbase;
+    a.abase = c.abase;
+    a.nb_max = (c.rmax + 127) / 128;
+    a.ns_max = (c.smax + 127) / 128;
+    a.wg_norm = std::min(kWgNormMax, std::max(1, c.sbmax));
+    a.io_dtype = dt == HIMUON_BF16 ? 0 : 1;
+    a.wk_dtype = G.wk;
+    a.muon = muon ? 1 : 0;
+    a.eps = eps;
+    a.normalize = normalize ? 1 : 0;
+    a.mu = mu;
+    a.eta = eta;
+    char* base = reinterpret_cast<char*>(ws);
+    const size_t xb = align_up((size_t)c.xel * es), ab = align_up((size_t)c.ael * es);
+    a.Xc = base;
+    a.Xn = base + xb;
+    for (int i = 0; i < nsq; ++i) sq[i] = base + 2 * xb + i * ab;
+    a.partial = reinterpret_cast<float*>(base + 2 * xb + nsq * ab);
+}
+
 himuon_status_t run(const std::vector<MatSpec>& specs, int32_t T, int32_t K, const float* abc,
                     himuon_dtype_t dt, float eps, float mu, float eta, bool muon, void* ws, size_t ws_bytes,
                     void* stream, bool normalize = true) {
@@ -434,36 +505,11 @@ himuon_status_t run(const std::vector<MatSpec>& specs, int32_t T, int32_t K, con
     }
 
     for (const Chunk& c : plan.chunks) {
-        const Group& G = plan.sgroups[c.group];
-        const size_t es = G.wk == 0 ? 2 : 4;
         StepArgs a{};
-        a.nmats = (int32_t)G.cls.size();
-        for (size_t k = 0; k < G.cls.size(); ++k)
-            a.mats[k] = entry_of(specs[G.cls[k].spec], G.cls[k], G.tile_base[k], G.xoff[k], G.aoff[k]);
-        for (int i = 0; i < 3 * K; ++i) a.abc[i] = abc[i];
-        a.T = T;
-        a.K = K;
-        a.tile_begin = c.tb;
-        a.tile_end = c.te;
-        a.xbase = c.xbase;
-        a.abase = c.abase;
-        a.nb_max = (c.rmax + 127) / 128;
-        a.ns_max = (c.smax + 127) / 128;
-        a.wg_norm = std::min(kWgNormMax, std::max(1, c.sbmax));
-        a.io_dtype = dt == HIMUON_BF16 ? 0 : 1;
-        a.wk_dtype = G.wk;
-        a.muon = muon ? 1 : 0;
-        a.eps = eps;
-        a.normalize = normalize ? 1 : 0;
-        a.mu = mu;
-        a.eta = eta;
-        char* base = reinterpret_cast<char*>(ws);
-        const size_t xb = align_up((size_t)c.xel * es), ab = align_up((size_t)c.ael * es);
-        a.Xc = base;
-        a.Xn = base + xb;
-        a.A = base + 2 * xb;
-        a.B = base + 2 * xb + ab;
-        a.partial = reinterpret_cast<float*>(base + 2 * xb + 2 * ab);
+        char* sq[2];
+        chunk_args(specs, plan, c, T, K, abc, dt, eps, mu, eta, muon, normalize, ws, 2, a, sq);
+        a.A = sq[0];
+        a.B = sq[1];
         const int64_t nt = c.te - c.tb;
         hipError_t e = launch_step_norm(a, s);
         if (e != hipSuccess) return hip_fail(e);
@@ -477,6 +523,104 @@ himuon_status_t run(const std::vector<MatSpec>& specs, int32_t T, int32_t K, con
             if ((e = launch_step_apply(a, s)) != hipSuccess) return hip_fail(e);
             std::swap(a.Xc, a.Xn);
         }
+    }
+    return HIMUON_OK;
+}
+
+// Tile edge that makes every matrix one tile: the largest side of the batch
+// (1 when there is nothing to look at; gather reports bad descriptors).  0 if
+// a side does not fit the int32 tile grid.
+int32_t whole_tile(const himuon_matrix_t* m, int32_t n) {
+    int64_t T = 1;
+    for (int32_t i = 0; m != nullptr && i < n; ++i) T = std::max({T, m[i].rows, m[i].cols});
+    return T > INT32_MAX ? 0 : (int32_t)T;
+}
+
+// Gram Newton-Schulz ("Gram Newton-Schulz" summary page, section 6,
+// Algorithm 3) on every matrix as one tile, oriented so that r <= s.  The
+// iteration runs on r x r matrices: R = X X^T, per step t
+//     P = a_t I + b_t R + c_t R^2,  Q <- P Q,  R <- P R P,
+// which is the page's Z, Q, RZ and R update with the identity terms folded
+// into P (every matrix here is a polynomial in the same symmetric R, so the
+// products commute and each result is symmetric: only lower blocks are
+// computed and mirrored).  A restart before step restart + 1 applies Q to X,
+// rebuilds R from it and starts Q again from I; at the end X <- Q X is
+// written in place.  Four r x r areas rotate: R, P, Q and a spare.
+himuon_status_t run_gram(const std::vector<MatSpec>& specs, int32_t T, int32_t K, const float* abc,
+                         int32_t restart, himuon_dtype_t dt, float eps, void* ws, size_t ws_bytes, void* stream) {
+    if (specs.empty()) return HIMUON_OK;
+    if (ws_bytes > 0 && ws == nullptr) return HIMUON_ERR_WORKSPACE;
+    Plan plan;
+    himuon_status_t st = build_plan(specs, T, K, dt, ws_bytes, true, plan, true, restart);
+    if (st != HIMUON_OK) return st;
+    if (!plan.chunks.empty() && ws == nullptr) return HIMUON_ERR_WORKSPACE;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    for (const Chunk& c : plan.chunks) {
+        StepArgs a{};
+        char* sq[4];
+        chunk_args(specs, plan, c, T, K, abc, dt, eps, 0.f, 0.f, false, true, ws, 4, a, sq);
+        const int64_t nt = c.te - c.tb;
+        const int64_t tri = (int64_t)a.nb_max * (a.nb_max + 1) / 2;
+        const int32_t sym_grid = (int32_t)(((nt * tri) + 7) / 8 * 8);
+        const int32_t apply_grid = (int32_t)(((nt * a.nb_max * a.ns_max) + 7) / 8 * 8);
+        void* const R = sq[0];
+        // one of the other three areas that holds neither x nor y
+        auto other = [&](const void* x, const void* y) -> void* {
+            for (int i = 1; i < 4; ++i)
+                if (sq[i] != x && sq[i] != y) return sq[i];
+            return nullptr;
+        };
+        auto product = [&](const void* L, const void* M, void* O) {   // O = L M^T
+            a.L = L;
+            a.M = M;
+            a.O = O;
+            a.grid_blocks = sym_grid;
+            return launch_step_product(a, s);
+        };
+        auto gram_of_x = [&]() {   // R = X X^T
+            a.A = R;
+            a.grid_blocks = sym_grid;
+            return launch_step_gram(a, s);
+        };
+        auto apply_q = [&](void* Q, int32_t step) {   // X <- Q X (written in place when step == K - 1)
+            a.B = Q;
+            a.step = step;
+            a.grid_blocks = apply_grid;
+            hipError_t e = launch_step_apply(a, s);
+            std::swap(a.Xc, a.Xn);
+            return e;
+        };
+        hipError_t e = launch_step_norm(a, s);
+        if (e == hipSuccess) e = gram_of_x();
+        void* Q = nullptr;   // nullptr: the identity
+        for (int32_t t = 1; t <= K && e == hipSuccess; ++t) {
+            if (restart > 0 && t == restart + 1) {
+                if ((e = apply_q(Q, t - 2)) != hipSuccess) break;
+                if ((e = gram_of_x()) != hipSuccess) break;
+                Q = nullptr;
+            }
+            // P = a I + b R + c R^2 (step t's coefficients)
+            void* P = other(Q, nullptr);
+            a.A = R;
+            a.B = P;
+            a.step = t - 1;
+            a.grid_blocks = sym_grid;
+            if ((e = launch_step_poly(a, s)) != hipSuccess) break;
+            if (Q == nullptr) {
+                Q = P;
+            } else {
+                void* Qn = other(P, Q);
+                if ((e = product(P, Q, Qn)) != hipSuccess) break;
+                Q = Qn;
+            }
+            if (t < K && !(restart > 0 && t == restart)) {
+                void* Tm = other(P, Q);   // R P, then R <- P (R P)
+                if ((e = product(R, P, Tm)) != hipSuccess) break;
+                if ((e = product(P, Tm, R)) != hipSuccess) break;
+            }
+        }
+        if (e == hipSuccess) e = apply_q(Q, K - 1);
+        if (e != hipSuccess) return hip_fail(e);
     }
     return HIMUON_OK;
 }
@@ -612,6 +756,39 @@ himuon_status_t himuon_muon_step(const himuon_matrix_t* W, const himuon_matrix_t
     return run(specs, T, K, abc, dt, eps, mu, eta, true, workspace, workspace_bytes, stream);
 }
 
+himuon_status_t himuon_gram_ns_workspace(const himuon_matrix_t* m, int32_t n, himuon_dtype_t dt, size_t* full,
+                                         size_t* min) {
+    if (full) *full = 0;
+    if (min) *min = 0;
+    himuon_status_t st = check_common(n, 1, 0, dt, 0.f);
+    if (st != HIMUON_OK) return st;
+    std::vector<MatSpec> specs;
+    const int32_t T = whole_tile(m, n);
+    if (T == 0) return HIMUON_ERR_LAYOUT;
+    if ((st = gather(nullptr, m, nullptr, n, T, dt, specs)) != HIMUON_OK) return st;
+    Plan plan;
+    if ((st = build_plan(specs, T, 1, dt, 0, false, plan, true, 0)) != HIMUON_OK) return st;
+    if (full) *full = plan.ws_full;
+    if (min) *min = plan.ws_min;
+    return HIMUON_OK;
+}
+
+himuon_status_t himuon_gram_ns(const himuon_matrix_t* m, int32_t n, int32_t K, const float* abc, int32_t restart,
+                               himuon_dtype_t dt, float eps, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+    if (restart < 0) return HIMUON_ERR_INVALID_ARGUMENT;
+    himuon_status_t st = check_common(n, 1, K, dt, eps);
+    if (st != HIMUON_OK) return st;
+    if ((st = check_abc(K, abc)) != HIMUON_OK) return st;
+    std::vector<MatSpec> specs;
+    const int32_t T = whole_tile(m, n);
+    if (T == 0) return HIMUON_ERR_LAYOUT;
+    if ((st = gather(nullptr, m, nullptr, n, T, dt, specs)) != HIMUON_OK) return st;
+    // K = 0 is the normalisation alone, which the standard path writes
+    if (K == 0) return run(specs, T, 0, abc, dt, eps, 0.f, 0.f, false, workspace, workspace_bytes, stream);
+    return run_gram(specs, T, K, abc, restart >= K ? 0 : restart, dt, eps, workspace, workspace_bytes, stream);
+}
+
 himuon_status_t himuon_pair_stats_workspace(const himuon_matrix_t* a, int32_t n, size_t* bytes) {
     if (bytes == nullptr) return HIMUON_ERR_INVALID_ARGUMENT;
     int64_t total = 0;
@@ -690,6 +867,6 @@ const char* himuon_status_string(himuon_status_t s) {
 
 int32_t himuon_last_hip_error(void) { return g_last_hip; }
 
-int32_t himuon_version(void) { return 10200; }
+int32_t himuon_version(void) { return 10300; }
 
 }  // extern "C"

@@ -67,6 +67,11 @@ struct StepArgs {
     void* A;                    // Gram matrices A = X X^T
     void* B;                    // B' = a I + b A + c A^2
     float* partial;             // wg_norm partial sums of squares per tile
+    // product of two r x r matrices with a symmetric result, O = L M^T (Gram
+    // iteration); same layout and offsets as A
+    const void* L;
+    const void* M;
+    void* O;
 };
 
 // Index of the class holding tile t: the last entry with tile_base <= t
@@ -122,5 +127,6 @@ hipError_t launch_step_norm(const StepArgs& a, hipStream_t s);
 hipError_t launch_step_gram(const StepArgs& a, hipStream_t s);
 hipError_t launch_step_poly(const StepArgs& a, hipStream_t s);
 hipError_t launch_step_apply(const StepArgs& a, hipStream_t s);
+hipError_t launch_step_product(const StepArgs& a, hipStream_t s);
 
 }  // namespace himuon

@@ -254,6 +254,10 @@ __global__ __launch_bounds__(256) void step_norm_kernel(const StepArgs a) {
 // MODE 0 gram:  C = X X^T          (r x r, contraction over s), lower blocks
 // MODE 1 poly:  C = A A, B' = a I + b A + c C                   lower blocks
 // MODE 2 apply: C = B' X           (r x s, contraction over r)
+// MODE 3 product: C = L M^T        (r x r, contraction over r), lower blocks;
+//                 for results known to be symmetric (products of matrices
+//                 that commute, as in the Gram iteration); the diagonal
+//                 blocks keep their lower triangle, so C is exactly symmetric
 // bf16: v_mfma_f32_32x32x16_bf16, k chunk 64; fp32: v_mfma_f32_32x32x2f32,
 // k chunk 32; two LDS stages.  Row operands are read from LDS along k; the X
 // operand of apply (k along rows of X) uses ds_read_tr16_b64 for bf16.
@@ -326,14 +330,14 @@ __device__ __forceinline__ void gemm_epilogue(const StepArgs& a, const TileRef& 
                 float v[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * m + e];
-                if (MODE == 0 || MODE == 1) {
+                if (MODE != 2) {
                     // columns up to the padded row length are written: past r
                     // the product is exactly zero (zero operand rows), which
                     // keeps the padding of A and B' zero for readers that do not
                     // mask it
                     const int64_t ld = round8(g.r);
                     if (col >= ld) continue;
-                    ET* Out = reinterpret_cast<ET*>(MODE == 0 ? a.A : a.B) + g.aoff;
+                    ET* Out = reinterpret_cast<ET*>(MODE == 0 ? a.A : MODE == 1 ? a.B : a.O) + g.aoff;
                     if (MODE == 1) {
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
@@ -347,6 +351,21 @@ __device__ __forceinline__ void gemm_epilogue(const StepArgs& a, const TileRef& 
                     ET o[4];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) o[e] = E::cv(v[e]);
+                    if (MODE == 3 && bm == bn) {
+                        // diagonal block of a product of two different
+                        // matrices: its two triangles differ by rounding, so
+                        // the lower one is kept and mirrored and the stored
+                        // result is exactly symmetric (padding columns get
+                        // their zeros directly)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int rr = row0 + e;
+                            if (rr >= g.r) continue;
+                            if (rr >= col || col >= g.r) Out[(int64_t)rr * ld + col] = o[e];
+                            if (rr > col) Out[(int64_t)col * ld + rr] = o[e];
+                        }
+                        continue;
+                    }
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
                         if (row0 + e < g.r) Out[(int64_t)(row0 + e) * ld + col] = o[e];
@@ -439,6 +458,10 @@ __global__ __launch_bounds__(256) void step_gemm_kernel(const StepArgs a) {
     } else if (MODE == 1) {
         P = reinterpret_cast<const ET*>(a.A) + g.aoff; ldp = round8(g.r);
         Q = P; ldq = ldp;
+        prow = g.r; kdim = g.r; qrow = g.r; qcol = 0;
+    } else if (MODE == 3) {
+        P = reinterpret_cast<const ET*>(a.L) + g.aoff; ldp = round8(g.r);
+        Q = reinterpret_cast<const ET*>(a.M) + g.aoff; ldq = ldp;
         prow = g.r; kdim = g.r; qrow = g.r; qcol = 0;
     } else {
         P = reinterpret_cast<const ET*>(a.B) + g.aoff; ldp = round8(g.r);
@@ -695,6 +718,10 @@ __global__ __launch_bounds__(256) void step_gemm_async(const StepArgs a) {
         P = reinterpret_cast<const ET*>(a.A) + g.aoff; ldp = (int)round8(g.r);
         Q = P; ldq = ldp;
         prow = g.r; kdim = g.r; qrows = g.r; qcol = 0;
+    } else if (MODE == 3) {
+        P = reinterpret_cast<const ET*>(a.L) + g.aoff; ldp = (int)round8(g.r);
+        Q = reinterpret_cast<const ET*>(a.M) + g.aoff; ldq = ldp;
+        prow = g.r; kdim = g.r; qrows = g.r; qcol = 0;
     } else {
         P = reinterpret_cast<const ET*>(a.B) + g.aoff; ldp = (int)round8(g.r);
         Q = reinterpret_cast<const ET*>(a.Xc) + g.xoff; ldq = (int)round8(g.s);
@@ -855,6 +882,20 @@ __global__ __launch_bounds__(256) void step_gemm_async(const StepArgs a) {
             for (int q = 0; q < 16; ++q)
                 sbuf[sw(wm * 64 + i * 32 + (q >> 2) * 8 + gl * 4 + (q & 3), wn * 64 + j * 32 + l32)] = cv[i][j][q];
     __syncthreads();
+    if (MODE == 3 && bm == bn) {
+        // diagonal block of a product of two different matrices: its two
+        // triangles differ by rounding, so the lower one is copied over the
+        // upper one and the stored result is exactly symmetric (the Gram
+        // iteration amplifies any asymmetry); reads are strictly below the
+        // diagonal, writes strictly above
+#pragma unroll 4
+        for (int it = 0; it < 64; ++it) {
+            const int id = it * 256 + tid;
+            const int R = id >> 7, c = id & 127;
+            if (c > R) sbuf[sw(R, c)] = sbuf[sw(c, R)];
+        }
+        __syncthreads();
+    }
     if (MODE == 2 && last) {
         // the result goes in place into the matrix (bf16), oriented back: a
         // tall tile was stored transposed, so its C^T block is written; the
@@ -915,7 +956,7 @@ __global__ __launch_bounds__(256) void step_gemm_async(const StepArgs a) {
         rows_ok = g.r;
         cols_ok = (int)round8(g.s);
     } else {
-        Out = reinterpret_cast<ET*>(MODE == 0 ? a.A : a.B) + g.aoff;
+        Out = reinterpret_cast<ET*>(MODE == 0 ? a.A : MODE == 1 ? a.B : a.O) + g.aoff;
         ldo = round8(g.r);
         rows_ok = g.r;
         cols_ok = (int)round8(g.r);   // past r the values are zero: the padding stays zero
@@ -993,5 +1034,6 @@ static hipError_t launch_gemm(const StepArgs& a, hipStream_t s) {
 hipError_t launch_step_gram(const StepArgs& a, hipStream_t s) { return launch_gemm<0>(a, s); }
 hipError_t launch_step_poly(const StepArgs& a, hipStream_t s) { return launch_gemm<1>(a, s); }
 hipError_t launch_step_apply(const StepArgs& a, hipStream_t s) { return launch_gemm<2>(a, s); }
+hipError_t launch_step_product(const StepArgs& a, hipStream_t s) { return launch_gemm<3>(a, s); }
 
 }  // namespace himuon
