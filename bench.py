@@ -1,6 +1,7 @@
 """Throughput of the HiMuon tiled Newton-Schulz step on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--T T]
+    python bench.py --gram [--restart 2] --workload NAME   # full map through the Gram iteration
 
 A step is one himuon_tiled_ns call over the whole workload (all matrices of
 the batch, every tile, all K Newton-Schulz steps), with the inputs already
@@ -216,6 +217,109 @@ def pair_stats_bench(H, torch, w, mats, steps, warmup, no_cpu):
     return res
 
 
+def gram_flops(shapes, K, restart):
+    """Full-product flops of the Gram iteration per call, summed over the
+    matrices (r = shorter side, s = longer): R = X X^T and the final Q X
+    (2 r^2 s each), per step R^2 (2 r^3), the running product (2 r^3, not on
+    the first step after a start or restart) and the R update (4 r^3, not after
+    the last step nor before a restart), and per restart Q X and X X^T."""
+    tot = 0.0
+    for h, w in shapes:
+        r, s_ = float(min(h, w)), float(max(h, w))
+        f = 4.0 * r * r * s_
+        ident = True
+        for t in range(1, K + 1):
+            if restart and t == restart + 1:
+                f += 4.0 * r * r * s_
+                ident = True
+            f += 2.0 * r ** 3 + (0.0 if ident else 2.0 * r ** 3)
+            ident = False
+            if t < K and not (restart and t == restart):
+                f += 4.0 * r ** 3
+        tot += f
+    return tot
+
+
+def gram_bench(H, torch, w, mats, K, restart, steps, warmup, cap, no_cpu):
+    """Time himuon_gram_ns (the full-matrix map through the Gram iteration)
+    against himuon_tiled_ns with T = max(rows, cols) (the standard full map)
+    on the same matrices, each with its own workspace.  The value is the
+    standard map's algorithmic flops over the Gram call's time, so it compares
+    directly with the standard map's rate; the roofline is the Gram
+    iteration's own flops over its time."""
+    import workloads
+    shapes = [tuple(m.shape) for m in mats]
+    Tf = max(max(sh) for sh in shapes)
+    stream = torch.cuda.current_stream()
+    gfull, _ = H.himuon_gram_ns_workspace(mats)
+    gbytes = min(gfull, cap) if cap else gfull
+    gws = torch.empty(max(gbytes, 1), dtype=torch.uint8, device=mats[0].device)
+    sfull, _ = H.himuon_workspace_size(mats, Tf)
+    sbytes = min(sfull, cap) if cap else sfull
+    sws = torch.empty(max(sbytes, 1), dtype=torch.uint8, device=mats[0].device)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    ms_gram = timed(lambda: H.himuon_gram_ns(mats, K, workloads.COEFFS, restart=restart, workspace=gws,
+                                             workspace_bytes=gbytes, stream=stream))
+    ms_std = timed(lambda: H.himuon_tiled_ns(mats, Tf, K, workloads.COEFFS, workspace=sws,
+                                             workspace_bytes=sbytes, stream=stream))
+    alg_std = algorithmic_flops(shapes, Tf, K)
+    alg_gram = gram_flops(shapes, K, restart)
+    eff = alg_std / (ms_gram * 1e-3) / 1e12
+    own = alg_gram / (ms_gram * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
+    res = {
+        "metric": "full-matrix NS through the Gram iteration, standard-map TFLOP/s (2 r^2 (2s + r) K per matrix)",
+        "value": round(eff, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": round(ms_gram, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic (seeded normal entries, transformer-layer shapes)",
+        "config": {"workload": w.name + " full-matrix map, Gram iteration", "matrices": len(shapes), "K": K,
+                   "restart": restart, "workspace_bytes": gbytes, "parallelism": "single GPU"},
+        "standard_full_map_ms": round(ms_std, 5),
+        "speedup_vs_standard": round(ms_std / ms_gram, 3),
+        "flop_ratio_gram_over_standard": round(alg_gram / alg_std, 4),
+        "roofline": {"bound": "mfma", "achieved": round(own, 3), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(own / peak, 4), "traffic": None,
+                     "kernel": "whole call (step GEMMs of the Gram iteration)", "launch_ms": round(ms_gram, 5)},
+    }
+    if not no_cpu:
+        from oracle.gram_ns import gram_ns
+        i = max(range(len(shapes)), key=lambda k: min(shapes[k]) * max(shapes[k]))
+        h, w_ = shapes[i]
+        if min(h, w_) > 2048:
+            # a 2048-row (or -column) crop with the matrix's aspect ratio keeps
+            # the sample to seconds
+            f = 2048.0 / min(h, w_)
+            h, w_ = int(round(h * f)), int(round(w_ * f))
+        x = mats[i][:h, :w_].cpu().to(torch.float64).numpy()
+        n, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < 10.0 or n == 0:
+            gram_ns(x, [workloads.COEFFS] * K, restart=restart)
+            n += 1
+        dt = (time.perf_counter() - t0) / n
+        try:
+            from threadpoolctl import threadpool_info
+            threads = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
+        except Exception:
+            threads = os.cpu_count() or 1
+        res["cpu_baseline"] = {"value": round(algorithmic_flops([(h, w_)], max(h, w_), K) / dt / 1e12, 5),
+                               "unit": "TFLOP/s (standard-map count)", "cores": threads, "kind": "oracle",
+                               "sample": f"oracle gram_ns on the leading {h}x{w_} block of matrix {i} "
+                                         f"{shapes[i]}, {n} calls"}
+    return res
+
+
 def w_coeffs():
     import workloads
     return workloads.COEFFS
@@ -236,6 +340,10 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
     ap.add_argument("--pair-stats", action="store_true",
                     help="time the pair statistics (tiled-versus-full diagnostics) instead of the map")
+    ap.add_argument("--gram", action="store_true",
+                    help="time the full-matrix map through the Gram iteration (himuon_gram_ns) against the "
+                         "standard full map instead of the tiled map")
+    ap.add_argument("--restart", type=int, default=2, help="Gram iteration restart point (0: none)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB, 5 times (used to "
                          "calibrate the HBM byte counters)")
@@ -275,6 +383,10 @@ def main():
         print(json.dumps(pair_stats_bench(H, torch, w, mats, args.steps, args.warmup, args.no_cpu)), flush=True)
         return
     cap = args.cap if args.cap is not None else w.workspace_cap
+    if args.gram:
+        print(json.dumps(gram_bench(H, torch, w, mats, args.K, args.restart, args.steps, args.warmup, cap,
+                                    args.no_cpu)), flush=True)
+        return
     full, mn = H.himuon_workspace_size(mats, T)
     ws = None
     ws_bytes = 0
