@@ -834,6 +834,33 @@ __global__ __launch_bounds__(256) void step_gemm_async(const StepArgs a) {
         }
     };
 
+    // apply: the chunk's operands are read from LDS before the next chunk's
+    // loads are issued.  The compiler makes a transposed LDS read wait for
+    // every LDS load in flight (vmcnt 0), so reading after the issue would
+    // hold the products until the next chunk had landed.
+    auto read_nn = [&](const ET* cP, const ET* cQ, bf16x8 (&av)[BK / 16][2], bf16x8 (&bv)[BK / 16][2])
+        __attribute__((always_inline)) {
+#pragma unroll
+        for (int kk = 0; kk < BK / 16; ++kk) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int r = wm * 64 + i * 32 + l32;
+                const int pc = (kk * 2 + gl) ^ ((r >> SH) & (CPR - 1));
+                av[kk][i] = *reinterpret_cast<const bf16x8*>(&cP[r * BK + pc * 8]);
+            }
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int G = lane >> 4, i16 = lane & 15;
+                const int col = wn * 64 + j * 32 + 16 * (G & 1) + 4 * (i16 & 3);
+                const int row = kk * 16 + 8 * gl + (i16 >> 2);
+                const int off = row * 128 + (((col >> 3) ^ ((row & 3) * 4)) * 8) + (col & 7);
+                bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(&cQ[off]));
+                bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(&cQ[off + 4 * 128]));
+                bv[kk][j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            }
+        }
+    };
+
     // ---- pipeline: chunk kt + 1 in flight while kt is multiplied; one barrier
     //      per chunk (the barrier also tells that every wave is done with the
     //      stage the next loads overwrite) ----
@@ -844,8 +871,21 @@ __global__ __launch_bounds__(256) void step_gemm_async(const StepArgs a) {
         const int cur = kt & 1;
         __builtin_amdgcn_s_waitcnt(0u | (7u << 4) | (15u << 8));
         __syncthreads();
-        if (kt + 1 < nk) issue(kt + 1, cur ? sP0 : sP1, cur ? sQ0 : sQ1);
-        compute(kt, cur ? sP1 : sP0, cur ? sQ1 : sQ0);
+        if constexpr (NN) {
+            bf16x8 av[BK / 16][2], bv[BK / 16][2];
+            read_nn(cur ? sP1 : sP0, cur ? sQ1 : sQ0, av, bv);
+            if (kt + 1 < nk) issue(kt + 1, cur ? sP0 : sP1, cur ? sQ0 : sQ1);
+#pragma unroll
+            for (int kk = 0; kk < BK / 16; ++kk)
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[kk][i], bv[kk][j], acc[i][j], 0, 0, 0);
+        } else {
+            if (kt + 1 < nk) issue(kt + 1, cur ? sP0 : sP1, cur ? sQ0 : sQ1);
+            compute(kt, cur ? sP1 : sP0, cur ? sQ1 : sQ0);
+        }
     }
 
     const bool last = (MODE == 2) && (a.step == a.K - 1);
