@@ -286,6 +286,17 @@ __device__ __forceinline__ void store_out(const StepArgs& a, const MatEntry& me,
 #ifndef HIMUON_ASYNC_BK
 #define HIMUON_ASYNC_BK 32
 #endif
+// Chunks whose largest tile has at least this many 128-row blocks run the
+// 256 x 256 block shape (measured on MI355X: the symmetric products gain from
+// r = 1024 on, 13 % at r = 2048 and 38 % for X X^T of an 8192 x 28672 matrix;
+// the apply product is level at r = s = 2048, 8 % faster at 2048 x 5632 and
+// 16 % at 8192 x 28672, and 6 % slower at r = s = 1024)
+#ifndef HIMUON_STEP_BIG_NB_SYM
+#define HIMUON_STEP_BIG_NB_SYM 8
+#endif
+#ifndef HIMUON_STEP_BIG_NB_APPLY
+#define HIMUON_STEP_BIG_NB_APPLY 16
+#endif
 // k chunk of the step GEMMs (tuning knobs; multiples of 32)
 #ifndef HIMUON_STEP_BK_BF16
 #define HIMUON_STEP_BK_BF16 64
@@ -648,36 +659,71 @@ __global__ __launch_bounds__(256) void step_gemm_kernel(const StepArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// bf16 step GEMMs with direct global -> LDS loads (buffer_load ... lds): k
-// chunks of 32 in two LDS stages, the next chunk in flight while one is
-// multiplied.  With no register staging the kernel needs few VGPRs and 32 KB
-// of LDS, so several workgroups share a CU and hide each other's load
-// latency.  Loads are masked through the buffer range: a lane whose 16-byte
-// chunk lies outside the operand (rows past the tile, columns past the row)
-// gets an offset past the buffer's end and reads zeros.  The workspace's row
-// padding (up to a multiple of 8 elements) is kept zero by every writer, so
-// a chunk is either wholly valid or wholly outside.
+// bf16 step GEMMs with direct global -> LDS loads (buffer_load ... lds), in two
+// block shapes that share the code:
+//   128 x 128 output block: 4 waves of 64 x 64, 32 KB of LDS, several
+//     workgroups per CU;
+//   256 x 256 output block: 8 waves of 128 x 64, 64 KB of LDS, one workgroup
+//     per CU.  It moves half the bytes per flop from L2 into LDS (the CU's L1
+//     waiting on L2 is what bounds these GEMMs) and reads 0.75 KB of LDS
+//     operands per MFMA instead of 1 KB.
+// Both run k chunks of 32 in two LDS stages, the next chunk in flight while one
+// is multiplied, and accumulate every output element over k in the same
+// order, so they give the same bits.  Loads are masked through the buffer
+// range: a lane whose 16-byte chunk lies outside the operand (rows past the
+// tile, columns past the row) gets an offset past the buffer's end and reads
+// zeros.  The workspace's row padding (up to a multiple of 8 elements) is kept
+// zero by every writer, so a chunk is either wholly valid or wholly outside.
 // Stage layouts (dense, 16-byte chunks XOR-swizzled by row, so that both the
 // lane-contiguous DMA writes and the MFMA operand reads are conflict free):
-//   row panels (128 rows x 32):  chunk c of row r at position c ^ ((r >> 2) & 3)
-//   X panel of apply (32 x 128): chunk c of row r at position c ^ ((r & 3) * 4)
+//   row panels (block rows x 32): chunk c of row r at position c ^ ((r >> 2) & 3)
+//   X panel of apply (32 rows, in sub-panels of 128 columns): chunk c of row r
+//                                 at position c ^ ((r & 3) * 4)
+// The result goes out through LDS, 128 block rows at a time (rows padded by 8
+// elements, so each lane's stores are a base plus constant offsets and the
+// half-waves fall on different banks), as whole 16-byte row chunks; the
+// mirrored block of a symmetric product goes the same way from the transposed
+// rows.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-template <int MODE>
-__global__ __launch_bounds__(256) void step_gemm_async(const StepArgs a) {
-    using E = Elem<0>;
+template <bool BIG> struct AsyncShape;
+template <> struct AsyncShape<false> {
+    static constexpr int NT = 256, BE = 128, WNW = 2, FM = 2;
+};
+template <> struct AsyncShape<true> {
+    static constexpr int NT = 512, BE = 256, WNW = 4, FM = 4;
+};
+
+template <int MODE, bool BIG>
+__global__ __launch_bounds__(AsyncShape<BIG>::NT) void step_gemm_async(const StepArgs a) {
     using ET = unsigned short;
+    using S = AsyncShape<BIG>;
+    constexpr int NT = S::NT;                        // threads
+    constexpr int BE = S::BE;                        // output block edge
+    constexpr int WNW = S::WNW;                      // waves along n (two along m)
+    constexpr int FM = S::FM, FN = 2;                // 32 x 32 MFMA blocks of a wave along m and n
+    constexpr int WR = 32 * FM;                      // rows of a wave's tile (its columns: 64)
     constexpr int BK = HIMUON_ASYNC_BK;
-    constexpr int STAGE = 128 * BK;                  // elements per operand and stage
+    constexpr int STAGE = BE * BK;                   // elements per operand and stage
     constexpr int CPR = BK / 8;                      // 16-byte chunks per panel row
-    constexpr int NPI = CPR / 2;                     // DMA instructions per wave and operand
+    constexpr int NPI = BE * CPR / NT;               // DMA instructions per thread and operand
     constexpr int SH = CPR == 4 ? 2 : 1;             // row-panel swizzle: chunk ^ ((r >> SH) & (CPR - 1))
+    constexpr int PR = 128;                          // block rows per epilogue pass
+    constexpr int NPASS = BE / PR;
+    constexpr int CH = BE / 8;                       // 16-byte chunks per block row
+    constexpr int U = BE / 128;                      // 128-blocks per block edge
     static_assert(CPR == 4 || CPR == 8, "k chunk of 32 or 64");
+    static_assert(NPI * NT == BE * CPR, "the DMA instructions cover a panel");
+    constexpr int LDC = BE + 8;                      // LDS stride of the C rows of a pass
+    constexpr int LDT = PR + 8;                      // LDS stride of the transposed rows
+    constexpr int LDS_E = 4 * STAGE > PR * LDC ? (4 * STAGE > BE * LDT ? 4 * STAGE : BE * LDT)
+                                               : (PR * LDC > BE * LDT ? PR * LDC : BE * LDT);
     constexpr bool NN = MODE == 2;
-    __shared__ __attribute__((aligned(16))) ET sbuf[4 * STAGE];   // two stages of P and Q; the C tile
+    constexpr bool SYM = MODE != 2;
+    __shared__ __attribute__((aligned(16))) ET sbuf[LDS_E];   // two stages of P and Q; the C rows
     ET* const sP0 = sbuf;
     ET* const sP1 = sbuf + STAGE;
     ET* const sQ0 = sbuf + 2 * STAGE;
@@ -686,17 +732,18 @@ __global__ __launch_bounds__(256) void step_gemm_async(const StepArgs a) {
     // ---- workgroup -> (tile, block), blocks of one tile on one XCD ----
     const int nwg = a.grid_blocks;
     const int L = (blockIdx.x & 7) * (nwg >> 3) + (blockIdx.x >> 3);
-    const int bpt = NN ? a.nb_max * a.ns_max : a.nb_max * (a.nb_max + 1) / 2;
+    const int nbm = (a.nb_max + U - 1) / U, nsm = (a.ns_max + U - 1) / U;
+    const int bpt = NN ? nbm * nsm : nbm * (nbm + 1) / 2;
     const int tl = L / bpt, b = L - tl * bpt;
     const int t = a.tile_begin + tl;
     if (t >= a.tile_end) return;
     const TileRef tref = find_tile(a, t);
     const TileGeom& g = tref.g;
-    const int nb = (g.r + 127) / 128, ns = (g.s + 127) / 128;
+    const int nb = (g.r + BE - 1) / BE, ns = (g.s + BE - 1) / BE;
     int bm, bn;
     if (NN) {
-        bm = b / a.ns_max;
-        bn = b - bm * a.ns_max;
+        bm = b / nsm;
+        bn = b - bm * nsm;
         if (bm >= nb || bn >= ns) return;
     } else {
         bm = (int)((sqrtf(8.f * b + 1.f) - 1.f) * 0.5f);
@@ -705,7 +752,7 @@ __global__ __launch_bounds__(256) void step_gemm_async(const StepArgs a) {
         bn = b - bm * (bm + 1) / 2;
         if (bm >= nb) return;
     }
-    const int m0 = bm * 128, n0 = bn * 128;
+    const int m0 = bm * BE, n0 = bn * BE;
 
     const ET* P;
     const ET* Q;
@@ -734,10 +781,10 @@ __global__ __launch_bounds__(256) void step_gemm_async(const StepArgs a) {
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WNW, wn = wave % WNW;
     const int l32 = lane & 31, gl = lane >> 5;
 
-    // DMA source of instruction j of this wave (positions (2 wave + j) 64 + lane)
+    // DMA source of instruction j of this thread (LDS chunk (wave NPI + j) 64 + lane)
     int prow_j[NPI], pcol_j[NPI], qrow_j[NPI], qcol_j[NPI];
 #pragma unroll
     for (int j = 0; j < NPI; ++j) {
@@ -749,9 +796,10 @@ __global__ __launch_bounds__(256) void step_gemm_async(const StepArgs a) {
             qrow_j[j] = r;
             qcol_j[j] = pcol_j[j];
         } else {
-            const int rn = pos >> 4;
+            const int sub = pos / (BK * 16), pp = pos - sub * (BK * 16);
+            const int rn = pp >> 4;
             qrow_j[j] = rn;
-            qcol_j[j] = ((pos & 15) ^ ((rn & 3) * 4)) * 8;
+            qcol_j[j] = sub * 128 + ((pp & 15) ^ ((rn & 3) * 4)) * 8;
         }
     }
     auto issue = [&](int kt, ET* dP, ET* dQ) __attribute__((always_inline)) {
@@ -773,58 +821,49 @@ __global__ __launch_bounds__(256) void step_gemm_async(const StepArgs a) {
         }
     };
 
-    f32x16 acc[2][2];
+    f32x16 acc[FM][FN];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
-    unsigned avp[2][2][8];   // poly: A over the output block, bf16 pairs
+        for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
+    unsigned avp[FM][FN][8];   // poly: A over the output block, bf16 pairs
 
+    // symmetric products: both operands are row panels
     auto compute = [&](int kt, const ET* cP, const ET* cQ) __attribute__((always_inline)) {
 #pragma unroll
         for (int kk = 0; kk < BK / 16; ++kk) {
-            bf16x8 av[2], bv[2];
+            bf16x8 av[FM], bv[FN];
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int r = wm * 64 + i * 32 + l32;
+            for (int i = 0; i < FM; ++i) {
+                const int r = wm * WR + i * 32 + l32;
                 const int pc = (kk * 2 + gl) ^ ((r >> SH) & (CPR - 1));
                 av[i] = *reinterpret_cast<const bf16x8*>(&cP[r * BK + pc * 8]);
             }
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                if (!NN) {
-                    const int r = wn * 64 + j * 32 + l32;
-                    const int pc = (kk * 2 + gl) ^ ((r >> SH) & (CPR - 1));
-                    bv[j] = *reinterpret_cast<const bf16x8*>(&cQ[r * BK + pc * 8]);
-                } else {
-                    const int G = lane >> 4, i16 = lane & 15;
-                    const int col = wn * 64 + j * 32 + 16 * (G & 1) + 4 * (i16 & 3);
-                    const int row = kk * 16 + 8 * gl + (i16 >> 2);
-                    const int off = row * 128 + (((col >> 3) ^ ((row & 3) * 4)) * 8) + (col & 7);
-                    bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(&cQ[off]));
-                    bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(&cQ[off + 4 * 128]));
-                    bv[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-                }
+            for (int j = 0; j < FN; ++j) {
+                const int r = wn * 64 + j * 32 + l32;
+                const int pc = (kk * 2 + gl) ^ ((r >> SH) & (CPR - 1));
+                bv[j] = *reinterpret_cast<const bf16x8*>(&cQ[r * BK + pc * 8]);
             }
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < FM; ++i)
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
+                for (int j = 0; j < FN; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
         }
         if constexpr (MODE == 1) {
             // A over this output block is the k range [n0 + wn 64 + j 32, +32)
             // of the row panel (A symmetric): one k chunk
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
+            for (int j = 0; j < FN; ++j) {
                 const int c0 = n0 + wn * 64 + j * 32;
                 if (kt == c0 / BK) {
                     const int cl = c0 - kt * BK + l32;
 #pragma unroll
-                    for (int i = 0; i < 2; ++i)
+                    for (int i = 0; i < FM; ++i)
 #pragma unroll
                         for (int q = 0; q < 16; ++q) {
-                            const int r = wm * 64 + i * 32 + (q >> 2) * 8 + gl * 4 + (q & 3);
+                            const int r = wm * WR + i * 32 + (q >> 2) * 8 + gl * 4 + (q & 3);
                             const int pc = (cl >> 3) ^ ((r >> SH) & (CPR - 1));
                             const unsigned v = cP[r * BK + pc * 8 + (cl & 7)];
                             avp[i][j][q >> 1] = (q & 1) ? (avp[i][j][q >> 1] | (v << 16)) : v;
@@ -838,22 +877,23 @@ __global__ __launch_bounds__(256) void step_gemm_async(const StepArgs a) {
     // loads are issued.  The compiler makes a transposed LDS read wait for
     // every LDS load in flight (vmcnt 0), so reading after the issue would
     // hold the products until the next chunk had landed.
-    auto read_nn = [&](const ET* cP, const ET* cQ, bf16x8 (&av)[BK / 16][2], bf16x8 (&bv)[BK / 16][2])
+    auto read_nn = [&](const ET* cP, const ET* cQ, bf16x8 (&av)[BK / 16][FM], bf16x8 (&bv)[BK / 16][FN])
         __attribute__((always_inline)) {
 #pragma unroll
         for (int kk = 0; kk < BK / 16; ++kk) {
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int r = wm * 64 + i * 32 + l32;
+            for (int i = 0; i < FM; ++i) {
+                const int r = wm * WR + i * 32 + l32;
                 const int pc = (kk * 2 + gl) ^ ((r >> SH) & (CPR - 1));
                 av[kk][i] = *reinterpret_cast<const bf16x8*>(&cP[r * BK + pc * 8]);
             }
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
+            for (int j = 0; j < FN; ++j) {
                 const int G = lane >> 4, i16 = lane & 15;
                 const int col = wn * 64 + j * 32 + 16 * (G & 1) + 4 * (i16 & 3);
                 const int row = kk * 16 + 8 * gl + (i16 >> 2);
-                const int off = row * 128 + (((col >> 3) ^ ((row & 3) * 4)) * 8) + (col & 7);
+                const int sub = col >> 7, cl = col & 127;
+                const int off = sub * (BK * 128) + row * 128 + (((cl >> 3) ^ ((row & 3) * 4)) * 8) + (cl & 7);
                 bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(&cQ[off]));
                 bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(&cQ[off + 4 * 128]));
                 bv[kk][j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -872,15 +912,15 @@ __global__ __launch_bounds__(256) void step_gemm_async(const StepArgs a) {
         __builtin_amdgcn_s_waitcnt(0u | (7u << 4) | (15u << 8));
         __syncthreads();
         if constexpr (NN) {
-            bf16x8 av[BK / 16][2], bv[BK / 16][2];
+            bf16x8 av[BK / 16][FM], bv[BK / 16][FN];
             read_nn(cur ? sP1 : sP0, cur ? sQ1 : sQ0, av, bv);
             if (kt + 1 < nk) issue(kt + 1, cur ? sP0 : sP1, cur ? sQ0 : sQ1);
 #pragma unroll
             for (int kk = 0; kk < BK / 16; ++kk)
 #pragma unroll
-                for (int i = 0; i < 2; ++i)
+                for (int i = 0; i < FM; ++i)
 #pragma unroll
-                    for (int j = 0; j < 2; ++j)
+                    for (int j = 0; j < FN; ++j)
                         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[kk][i], bv[kk][j], acc[i][j], 0, 0, 0);
         } else {
             if (kt + 1 < nk) issue(kt + 1, cur ? sP0 : sP1, cur ? sQ0 : sQ1);
@@ -890,85 +930,73 @@ __global__ __launch_bounds__(256) void step_gemm_async(const StepArgs a) {
 
     const bool last = (MODE == 2) && (a.step == a.K - 1);
 
-    // ---- epilogue through LDS: the 128x128 bf16 block C (row-major, 16-byte
-    //      chunks XOR-swizzled by row), then whole 16-byte row chunks to the
-    //      workspace; the mirrored block of the symmetric products goes the
-    //      same way from C^T ----
+    // ---- epilogue through LDS, one pass per 128 block rows: the rows (bf16,
+    //      padded stride), then whole 16-byte row chunks to the workspace; a
+    //      symmetric product's mirrored part goes the same way from the
+    //      transposed rows ----
     const float ca = a.abc[3 * a.step], cb = a.abc[3 * a.step + 1], cc = a.abc[3 * a.step + 2];
-    auto sw = [](int row, int col) { return row * 128 + (((col >> 3) ^ (row & 15)) << 3) + (col & 7); };
-    unsigned short cv[2][2][16];
+    auto sw = [](int row, int col) { return row * LDC + col; };
+    auto swt = [](int row, int col) { return row * LDT + col; };
+    // the result rounded to bf16, two rows a register: cvp[i][j][p] holds rows
+    // 2p and 2p + 1 of the lane's 16 (the MFMA's register order)
+    unsigned cvp[FM][FN][8];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < FN; ++j)
 #pragma unroll
             for (int q = 0; q < 16; ++q) {
                 float v = acc[i][j][q];
                 if constexpr (MODE == 1) {
                     const float av = (q & 1) ? hi_f(avp[i][j][q >> 1]) : lo_f(avp[i][j][q >> 1]);
                     v = __builtin_fmaf(cc, v, cb * av);
-                    const int row = m0 + wm * 64 + i * 32 + (q >> 2) * 8 + gl * 4 + (q & 3);
+                    const int row = m0 + wm * WR + i * 32 + (q >> 2) * 8 + gl * 4 + (q & 3);
                     const int col = n0 + wn * 64 + j * 32 + l32;
                     if (row == col && col < g.r) v += ca;
                 }
-                cv[i][j][q] = f2bf(v);
+                const unsigned u = f2bf(v);
+                cvp[i][j][q >> 1] = (q & 1) ? (cvp[i][j][q >> 1] | (u << 16)) : u;
             }
-    __syncthreads();   // every wave is done with the k stages
+    // the waves whose rows lie in pass h write them (transposed when tr)
+    auto put_rows = [&](int h, bool tr) __attribute__((always_inline)) {
+        if (wm * WR < h * PR || wm * WR >= (h + 1) * PR) return;
+        const int rb = wm * WR - h * PR;
+        if (!tr) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+                for (int j = 0; j < FN; ++j)
 #pragma unroll
-            for (int q = 0; q < 16; ++q)
-                sbuf[sw(wm * 64 + i * 32 + (q >> 2) * 8 + gl * 4 + (q & 3), wn * 64 + j * 32 + l32)] = cv[i][j][q];
-    __syncthreads();
-    if (MODE == 3 && bm == bn) {
-        // diagonal block of a product of two different matrices: its two
-        // triangles differ by rounding, so the lower one is copied over the
-        // upper one and the stored result is exactly symmetric (the Gram
-        // iteration amplifies any asymmetry); reads are strictly below the
-        // diagonal, writes strictly above
-#pragma unroll 4
-        for (int it = 0; it < 64; ++it) {
-            const int id = it * 256 + tid;
-            const int R = id >> 7, c = id & 127;
-            if (c > R) sbuf[sw(R, c)] = sbuf[sw(c, R)];
+                    for (int q = 0; q < 16; ++q)
+                        sbuf[sw(rb + i * 32 + (q >> 2) * 8 + gl * 4 + (q & 3), wn * 64 + j * 32 + l32)] =
+                            (unsigned short)((q & 1) ? (cvp[i][j][q >> 1] >> 16) : (cvp[i][j][q >> 1] & 0xffffu));
+        } else {
+            // lane l holds rows rho .. rho+3 of column l%32: 4 consecutive
+            // elements of one transposed row (8-byte stores)
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        const int Rt = wn * 64 + j * 32 + l32;
+                        const int Ct = rb + i * 32 + m * 8 + gl * 4;
+                        const u32x2 pk = {cvp[i][j][2 * m], cvp[i][j][2 * m + 1]};
+                        *reinterpret_cast<u32x2*>(&sbuf[swt(Rt, Ct)]) = pk;
+                    }
         }
-        __syncthreads();
-    }
+    };
+
     if (MODE == 2 && last) {
         // the result goes in place into the matrix (bf16), oriented back: a
-        // tall tile was stored transposed, so its C^T block is written; the
-        // Muon variant updates W <- W - eta X instead
+        // tall tile was stored transposed, so its transposed rows are
+        // written; the Muon variant updates W <- W - eta X instead
         const MatEntry& me = a.mats[tref.mi];
         ET* base = reinterpret_cast<ET*>(a.muon ? me.w : me.m);
         const int64_t ld = a.muon ? me.w_ld : me.m_ld;
         const bool vec = vec_ok(base, ld, g.c0);
-        if (g.tr) {
-            __syncthreads();
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-#pragma unroll
-                    for (int m = 0; m < 4; ++m) {
-                        const int Rt = wn * 64 + j * 32 + l32;
-                        const int Ct = wm * 64 + i * 32 + m * 8 + gl * 4;
-                        u32x2 pk = {(unsigned)cv[i][j][4 * m] | ((unsigned)cv[i][j][4 * m + 1] << 16),
-                                    (unsigned)cv[i][j][4 * m + 2] | ((unsigned)cv[i][j][4 * m + 3] << 16)};
-                        *reinterpret_cast<u32x2*>(&sbuf[sw(Rt, Ct)]) = pk;
-                    }
-            __syncthreads();
-        }
-        // LDS block row R = tile row m0 + R (or, tall, tile column n0 + R)
-        const int rbase = g.tr ? n0 : m0, cbase = g.tr ? m0 : n0;
-#pragma unroll
-        for (int it = 0; it < 8; ++it) {
-            const int id = it * 256 + tid;
-            const int R = id >> 4, ch = id & 15;
-            const int orow = rbase + R, ocol = cbase + ch * 8;
-            if (orow >= g.h || ocol >= g.w) continue;
-            u16x8 v = *reinterpret_cast<const u16x8*>(&sbuf[sw(R, ch * 8)]);
+        auto put = [&](int orow, int ocol, u16x8 v) __attribute__((always_inline)) {
+            if (orow >= g.h || ocol >= g.w) return;
             ET* op = base + (int64_t)(g.r0 + orow) * ld + g.c0 + ocol;
             if (vec && ocol + 8 <= g.w) {
                 if (a.muon) {
@@ -984,9 +1012,33 @@ __global__ __launch_bounds__(256) void step_gemm_async(const StepArgs a) {
                     op[e] = a.muon ? f2bf(bf2f(op[e]) - a.eta * bf2f(v[e])) : v[e];
                 }
             }
+        };
+#pragma unroll
+        for (int h = 0; h < NPASS; ++h) {
+            __syncthreads();   // the k stages, or the previous pass, are done with
+            put_rows(h, g.tr != 0);
+            __syncthreads();
+            if (!g.tr) {
+                // LDS row R = tile row m0 + h PR + R
+#pragma unroll
+                for (int it = 0; it < PR * CH / NT; ++it) {
+                    const int id = it * NT + tid;
+                    const int R = id / CH, ch = id % CH;
+                    put(m0 + h * PR + R, n0 + ch * 8, *reinterpret_cast<const u16x8*>(&sbuf[sw(R, ch * 8)]));
+                }
+            } else {
+                // transposed LDS row R = tile column n0 + R
+#pragma unroll
+                for (int it = 0; it < BE * 16 / NT; ++it) {
+                    const int id = it * NT + tid;
+                    const int R = id >> 4, ch = id & 15;
+                    put(n0 + R, m0 + h * PR + ch * 8, *reinterpret_cast<const u16x8*>(&sbuf[swt(R, ch * 8)]));
+                }
+            }
         }
         return;
     }
+
     ET* Out;
     int64_t ldo;
     int rows_ok, cols_ok;
@@ -1001,38 +1053,54 @@ __global__ __launch_bounds__(256) void step_gemm_async(const StepArgs a) {
         rows_ok = g.r;
         cols_ok = (int)round8(g.r);   // past r the values are zero: the padding stays zero
     }
+    const bool diag = SYM && bm == bn;
 #pragma unroll
-    for (int it = 0; it < 8; ++it) {
-        const int id = it * 256 + tid;
-        const int R = id >> 4, ch = id & 15;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(&sbuf[sw(R, ch * 8)]);
-        if (m0 + R < rows_ok && n0 + ch * 8 < cols_ok)
-            *reinterpret_cast<u32x4*>(Out + (int64_t)(m0 + R) * ldo + n0 + ch * 8) = v;
-    }
-    if (MODE == 2 || bm == bn) return;
-    __syncthreads();
-    // C^T: lane l holds rows rho .. rho+3 of column l%32, i.e. 4 consecutive
-    // elements of one row of C^T (8-byte stores)
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const int Rt = wn * 64 + j * 32 + l32;
-                const int Ct = wm * 64 + i * 32 + m * 8 + gl * 4;
-                u32x2 pk = {(unsigned)cv[i][j][4 * m] | ((unsigned)cv[i][j][4 * m + 1] << 16),
-                            (unsigned)cv[i][j][4 * m + 2] | ((unsigned)cv[i][j][4 * m + 3] << 16)};
-                *reinterpret_cast<u32x2*>(&sbuf[sw(Rt, Ct)]) = pk;
+    for (int h = 0; h < NPASS; ++h) {
+        __syncthreads();   // the k stages, or the previous pass, are done with
+        put_rows(h, false);
+        __syncthreads();
+        if (MODE == 3 && diag) {
+            // the diagonal 128-block of this pass: the two triangles of a
+            // product of two different matrices differ by rounding, so the
+            // lower one is copied over the upper one and the stored result is
+            // exactly symmetric (the Gram iteration amplifies any asymmetry);
+            // reads are strictly below the diagonal, writes strictly above
+#pragma unroll 4
+            for (int it = 0; it < PR * PR / NT; ++it) {
+                const int id = it * NT + tid;
+                const int R = id >> 7, c = id & 127;
+                if (c > R) sbuf[sw(R, h * PR + c)] = sbuf[sw(c, h * PR + R)];
             }
-    __syncthreads();
+            __syncthreads();
+        }
+        // in a diagonal block, columns past this pass's diagonal 128-block are
+        // strictly above the diagonal: a later pass mirrors them
+        const int cmax = diag ? (h + 1) * PR : BE;
 #pragma unroll
-    for (int it = 0; it < 8; ++it) {
-        const int id = it * 256 + tid;
-        const int R = id >> 4, ch = id & 15;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(&sbuf[sw(R, ch * 8)]);
-        if (n0 + R < rows_ok && m0 + ch * 8 < cols_ok)
-            *reinterpret_cast<u32x4*>(Out + (int64_t)(n0 + R) * ldo + m0 + ch * 8) = v;
+        for (int it = 0; it < PR * CH / NT; ++it) {
+            const int id = it * NT + tid;
+            const int R = id / CH, ch = id % CH;
+            const u32x4 v = *reinterpret_cast<const u32x4*>(&sbuf[sw(R, ch * 8)]);
+            if (m0 + h * PR + R < rows_ok && n0 + ch * 8 < cols_ok && ch * 8 < cmax)
+                *reinterpret_cast<u32x4*>(Out + (int64_t)(m0 + h * PR + R) * ldo + n0 + ch * 8) = v;
+        }
+        if (!SYM) continue;
+        // mirror: transposed row c of this pass goes to row n0 + c, columns
+        // m0 + h PR ..; in a diagonal block only the columns left of this
+        // pass's diagonal 128-block (none in the first pass)
+        const int tmax = diag ? h * PR : BE;
+        if (tmax == 0) continue;
+        __syncthreads();
+        put_rows(h, true);
+        __syncthreads();
+#pragma unroll
+        for (int it = 0; it < BE * 16 / NT; ++it) {
+            const int id = it * NT + tid;
+            const int R = id >> 4, ch = id & 15;
+            const u32x4 v = *reinterpret_cast<const u32x4*>(&sbuf[swt(R, ch * 8)]);
+            if (R < tmax && n0 + R < rows_ok && m0 + h * PR + ch * 8 < cols_ok)
+                *reinterpret_cast<u32x4*>(Out + (int64_t)(n0 + R) * ldo + m0 + h * PR + ch * 8) = v;
+        }
     }
 }
 
@@ -1062,8 +1130,17 @@ static hipError_t launch_gemm(const StepArgs& a, hipStream_t s) {
     // the direct-to-LDS kernel addresses an operand with 32-bit byte offsets
     const int64_t rmax = 128LL * a.nb_max, smax = 128LL * a.ns_max;
     const bool small = rmax * std::max(rmax, smax) * 2 < (1LL << 31);
-    if (a.wk_dtype == 0 && small && HIMUON_STEP_ASYNC)
-        hipLaunchKernelGGL((step_gemm_async<MODE>), dim3(a.grid_blocks), dim3(256), 0, s, a);
+    const int big_nb = MODE == 2 ? HIMUON_STEP_BIG_NB_APPLY : HIMUON_STEP_BIG_NB_SYM;
+    if (a.wk_dtype == 0 && small && HIMUON_STEP_ASYNC && a.nb_max >= big_nb) {
+        // 256 x 256 blocks: the grid counts blocks of that size
+        StepArgs b = a;
+        const int64_t nt = a.tile_end - a.tile_begin;
+        const int64_t nbm = (a.nb_max + 1) / 2, nsm = (a.ns_max + 1) / 2;
+        const int64_t bpt = MODE == 2 ? nbm * nsm : nbm * (nbm + 1) / 2;
+        b.grid_blocks = (int32_t)((nt * bpt + 7) / 8 * 8);
+        hipLaunchKernelGGL((step_gemm_async<MODE, true>), dim3(b.grid_blocks), dim3(512), 0, s, b);
+    } else if (a.wk_dtype == 0 && small && HIMUON_STEP_ASYNC)
+        hipLaunchKernelGGL((step_gemm_async<MODE, false>), dim3(a.grid_blocks), dim3(256), 0, s, a);
     else if (a.wk_dtype == 0)
         hipLaunchKernelGGL((step_gemm_kernel<0, MODE>), dim3(a.grid_blocks), dim3(256), 0, s, a);
     else
