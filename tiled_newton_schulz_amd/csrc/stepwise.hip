@@ -689,6 +689,43 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void* base, uint
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
+// Output block (bm, bn) of linear block b within a tile, in groups of GM block
+// rows walked column by column, so that the workgroups that run at once share
+// both operands' k chunks in L2 (row-major order, GM = 1, shares only the row
+// panel and streams one column panel per workgroup: with long k that re-reads
+// every column panel from memory once per block row).  sym: the lower blocks
+// bn <= bm of an nbm x nbm grid; else the full nbm x nsm grid.
+__device__ __forceinline__ void grouped_block(int b, int nbm, int nsm, bool sym, int GM, int& bm, int& bn) {
+    if (!sym) {
+        const int per = GM * nsm;
+        const int grp = b / per, o = b - grp * per;
+        const int first = grp * GM, gm = min(GM, nbm - first);
+        bm = first + o % gm;
+        bn = o / gm;
+        return;
+    }
+    // group g holds rows [g GM, g GM + gm); the lower blocks of rows < r number
+    // r (r + 1) / 2
+    int first = 0;
+    while (first + GM < nbm && (first + GM) * (first + GM + 1) / 2 <= b) first += GM;
+    const int gm = min(GM, nbm - first);
+    int o = b - first * (first + 1) / 2;
+    if (o < first * gm) {   // columns left of the group's diagonal square: gm blocks each
+        bn = o / gm;
+        bm = first + o % gm;
+        return;
+    }
+    o -= first * gm;
+    // the group's diagonal square, column c holding rows c .. gm - 1
+    int c = 0;
+    while (o >= gm - c) {
+        o -= gm - c;
+        ++c;
+    }
+    bn = first + c;
+    bm = first + c + o;
+}
+
 template <bool BIG> struct AsyncShape;
 template <> struct AsyncShape<false> {
     static constexpr int NT = 256, BE = 128, WNW = 2, FM = 2;
@@ -740,18 +777,13 @@ __global__ __launch_bounds__(AsyncShape<BIG>::NT) void step_gemm_async(const Ste
     const TileRef tref = find_tile(a, t);
     const TileGeom& g = tref.g;
     const int nb = (g.r + BE - 1) / BE, ns = (g.s + BE - 1) / BE;
+    // groups pay where k is long (measured: the full map of an 8192 x 28672
+    // matrix fetches 2.8 times less past L2 and runs 8 % faster; with k = 2048
+    // row-major order is 6 % faster)
+    const int klen = MODE == 0 ? g.s : g.r;
     int bm, bn;
-    if (NN) {
-        bm = b / nsm;
-        bn = b - bm * nsm;
-        if (bm >= nb || bn >= ns) return;
-    } else {
-        bm = (int)((sqrtf(8.f * b + 1.f) - 1.f) * 0.5f);
-        while ((bm + 1) * (bm + 2) / 2 <= b) ++bm;
-        while (bm * (bm + 1) / 2 > b) --bm;
-        bn = b - bm * (bm + 1) / 2;
-        if (bm >= nb) return;
-    }
+    grouped_block(b, nbm, nsm, !NN, klen >= 4096 ? (BIG ? 4 : 8) : 1, bm, bn);
+    if (bm >= nb || bn >= ns) return;
     const int m0 = bm * BE, n0 = bn * BE;
 
     const ET* P;
