@@ -351,7 +351,7 @@ def main():
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the tiled map has no "
-              "cross-GPU exchange and this build measures one GPU's share", file=sys.stderr)
+              "exchange between GPUs, so one GPU's share is what is measured", file=sys.stderr)
         sys.exit(2)
 
     import torch

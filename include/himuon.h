@@ -74,7 +74,7 @@ typedef enum himuon_dtype {
 typedef enum himuon_status {
     HIMUON_OK = 0,
     HIMUON_ERR_INVALID_ARGUMENT = 1, /* null pointer, size < 1, ld < cols, K or eps out of range, non-finite coefficient */
-    HIMUON_ERR_UNSUPPORTED = 2,      /* dtype or option this build does not provide                                   */
+    HIMUON_ERR_UNSUPPORTED = 2,      /* dtype or option the library does not provide                                  */
     HIMUON_ERR_LAYOUT = 3,           /* pointer not aligned to the element size, or an index that overflows int64   */
     HIMUON_ERR_OVERLAP = 4,          /* two matrices that are written share memory                                  */
     HIMUON_ERR_WORKSPACE = 5,        /* workspace too small for one tile of the step-by-step path, or NULL with bytes > 0 */

@@ -20,7 +20,7 @@ Sources (cited by page title and section):
   the iteration applies a scalar odd polynomial to the singular values and keeps
   the singular vectors.
 
-Readings of points the pages leave open (each is listed in the design doc):
+Readings of points the pages leave open:
 
 * ragged edges: tiles are anchored at (0, 0); the last tile row/column holds the
   remainder and is processed at its own h x w size;

@@ -19,7 +19,7 @@ Per step t with (a, b, c) = (a_t, b_t, c_t):
 In exact arithmetic this is the standard map of the same page's Algorithm 1:
 with X_t = (a I + b R + c R^2) X_{t-1}, Q_t X_0 = X_t and R_t = X_t X_t^T.
 
-Readings (listed in DESIGN.md):
+Readings of points the page leaves open:
 * The listing ends with "X <- Q_4 X" after a five-step loop; the product of
   all steps run so far is applied (Q_5 for five steps), the only reading under
   which the iteration equals Algorithm 1.
