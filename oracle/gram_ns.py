@@ -20,9 +20,10 @@ In exact arithmetic this is the standard map of the same page's Algorithm 1:
 with X_t = (a I + b R + c R^2) X_{t-1}, Q_t X_0 = X_t and R_t = X_t X_t^T.
 
 Readings of points the page leaves open:
-* The listing ends with "X <- Q_4 X" after a five-step loop; the product of
-  all steps run so far is applied (Q_5 for five steps), the only reading under
-  which the iteration equals Algorithm 1.
+* After its five-step loop, Algorithm 3 applies the running product with the
+  index of step four.  The product of all steps run is applied here (step five's
+  for five steps), the only reading under which the iteration equals
+  Algorithm 1.
 * A tall block is transposed first so that R is the smaller Gram matrix (the
   page's input has n <= m); the result is transposed back.
 * restart = k restarts before step k + 1 (the page's t = 3 is restart = 2);
