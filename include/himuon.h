@@ -25,7 +25,10 @@
  *   vector fast path).
  * - The caller owns all device memory.  The library allocates no device memory
  *   and keeps no device state between calls.  The descriptor array and the
- *   coefficient array are read during the call only.
+ *   coefficient array are read during the call only.  A call issues kernel
+ *   launches only (no memsets or copies), so it may be captured in a HIP graph,
+ *   and calls on different streams may run at once on disjoint matrices and
+ *   workspaces.
  * - Work is enqueued on `stream` (a hipStream_t; NULL is the null stream) and
  *   the call returns without waiting.  Results are valid once the stream has
  *   reached that point.  The workspace must stay allocated until then.
