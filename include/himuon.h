@@ -46,7 +46,8 @@
  *   one for a partly filled last round of 128-tiles.  Larger tiles, thin
  *   tiles, fp32 data, and the full-matrix map (T >= max(rows, cols)) run step
  *   by step through the caller's workspace, in chunks of tiles that each fit
- *   in `workspace_bytes`.
+ *   in `workspace_bytes`; that workspace is bf16 for bf16 tiles whose sides
+ *   are both at least 64, fp32 otherwise.
  */
 #ifndef HIMUON_H
 #define HIMUON_H
@@ -204,7 +205,8 @@ himuon_status_t himuon_muon_step(const himuon_matrix_t* W, const himuon_matrix_t
  *              writes the normalised matrices as himuon_tiled_ns does).
  * stream     : hipStream_t to enqueue on.
  * The workspace holds the iterates in bf16 when dt is bf16 and both sides of
- * the matrix are at least 32, else in fp32.
+ * the matrix are at least 96, else in fp32 (smaller Gram matrices lose too
+ * much accuracy to bf16 rounding).
  * Errors: HIMUON_ERR_INVALID_ARGUMENT for restart < 0, otherwise as for
  * himuon_tiled_ns (HIMUON_ERR_LAYOUT also for a side above INT32_MAX).
  */

@@ -210,7 +210,7 @@ def route(th, tw):
         return "chip"
     if mx <= 64:
         return "chip-precise"
-    return "step-bf16" if mn >= 32 else "step-fp32"
+    return "step-bf16" if mn >= 64 else "step-fp32"
 
 
 def test_workspace_layout_closed_form():
@@ -328,13 +328,13 @@ def test_gram_ns_workspace_and_validation():
     """himuon_gram_ns: every matrix is one tile on the step path with two
     oriented X areas and four r x r areas (R, the step polynomial, the running
     product, a spare) plus the norm partials; bf16 keeps a bf16 workspace when
-    both sides are >= 32, else fp32.  Errors come before any launch."""
+    both sides are >= 96, else fp32.  Errors come before any launch."""
     al = lambda x: (x + 255) // 256 * 256
     r8 = lambda x: (x + 7) // 8 * 8
     for h, w, dt in [(2048, 5632, H.BF16), (5632, 2048, H.BF16), (300, 170, H.FP32), (20, 700, H.BF16),
                      (64, 64, H.BF16)]:
         r, s_ = min(h, w), max(h, w)
-        es = 4 if dt == H.FP32 or r < 32 else 2
+        es = 4 if dt == H.FP32 or r < 96 else 2
         want = 2 * al(es * r * r8(s_)) + 4 * al(es * r * r8(r)) + al(32 * 4)
         assert H.himuon_gram_ns_workspace([sd(h, w)], dt) == (want, want), (h, w)
     # several matrices: one chunk holds them all; min is the largest single one

@@ -116,9 +116,12 @@ himuon_status_t check_abc(int32_t K, const float* abc) {
 // share one shape, and each class is routed by that shape:
 //   bf16, both sides 32..256          -> on-chip kernel (kernel tile 32/64/128/256)
 //   bf16, a side < 32, both <= 64     -> on-chip kernel, hi/lo split precision
-//   bf16, both sides >= 32, one > 256 -> step path, bf16 workspace
-//   bf16, a side < 32, one > 64       -> step path, fp32 workspace
+//   bf16, both sides >= 64, one > 256 -> step path, bf16 workspace
+//   bf16, other thin tiles            -> step path, fp32 workspace
 //   fp32                              -> step path, fp32 workspace
+// (A bf16 iterate of a tile whose short side r is below 64 and whose long side
+// is long loses accuracy: emulated worst errors of 2.5-2.9e-2 for r = 32..40
+// and s = 600..2000 against 1.3e-2 at r = 64, with a 3e-2 bound.)
 struct TileClass {
     int spec;                 // matrix index
     int32_t ti0, tj0, n_ti, n_tj, th, tw;
@@ -132,7 +135,7 @@ Route route_of(himuon_dtype_t dt, int32_t th, int32_t tw) {
     if (dt == HIMUON_FP32) return Route::StepFp32;
     if (mx <= 256 && mn >= 32) return Route::OnChip;
     if (mx <= 64) return Route::OnChipPrecise;
-    if (mn >= 32) return Route::StepBf16;
+    if (mn >= 64) return Route::StepBf16;
     return Route::StepFp32;
 }
 int kernel_tile_for(int32_t th, int32_t tw) {
@@ -215,8 +218,10 @@ void oriented(const TileClass& c, int32_t& r, int32_t& sd) {
 // Builds the plan.  With enforce_cap, every chunk's workspace stays within
 // `cap` (HIMUON_ERR_WORKSPACE if one tile alone does not fit).  gram: every
 // tile runs the Gram iteration on the step path (restart as for
-// himuon_gram_ns); bf16 tiles with both sides >= 32 keep a bf16 workspace,
-// the others fp32.
+// himuon_gram_ns); bf16 tiles with both sides >= 96 keep a bf16 workspace,
+// the others fp32 (the r x r iterates of a bf16 Gram iteration lose accuracy
+// for small r: emulated worst errors of 3.3e-2 at r = 32, 2.9e-2 at 48,
+// 2.0e-2 at 64 and at most 1.3e-2 from 96 on, with a 3e-2 bound).
 himuon_status_t build_plan(const std::vector<MatSpec>& specs, int32_t T, int32_t K, himuon_dtype_t dt,
                            size_t cap, bool enforce_cap, Plan& plan, bool gram = false, int32_t restart = 0) {
     plan = Plan();
@@ -228,7 +233,7 @@ himuon_status_t build_plan(const std::vector<MatSpec>& specs, int32_t T, int32_t
 
     // step path workspace dtype of a class: 0 bf16, 1 fp32, -1 on chip
     auto step_wk = [&](const TileClass& c) {
-        if (gram) return (dt == HIMUON_FP32 || std::min(c.th, c.tw) < 32) ? 1 : 0;
+        if (gram) return (dt == HIMUON_FP32 || std::min(c.th, c.tw) < 96) ? 1 : 0;
         const Route r = route_of(dt, c.th, c.tw);
         return r == Route::StepBf16 ? 0 : r == Route::StepFp32 ? 1 : -1;
     };
