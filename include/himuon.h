@@ -39,9 +39,9 @@
  * - Matrices of one call must not overlap in memory (they are written in
  *   place).  No exception crosses this interface.
  * - Non-finite inputs are not an error: a NaN or Inf stays inside its tile.
- * - bf16 tiles with both sides at least 32 and at most 256 (and tiles with
- *   both sides at most 64) stay resident on chip for all K steps and need no
- *   workspace: one kernel launch per group of up to 256 tile classes (a class
+ * - bf16 tiles with both sides from 48 to 256 or from 32 to 128 (and tiles
+ *   with both sides at most 64) stay resident on chip for all K steps and
+ *   need no workspace: one kernel launch per group of up to 256 tile classes (a class
  *   is one matrix's interior, right-edge, bottom-edge or corner tiles), plus
  *   one for a partly filled last round of 128-tiles.  Larger tiles, thin
  *   tiles, fp32 data, and the full-matrix map (T >= max(rows, cols)) run step

@@ -206,7 +206,7 @@ def test_plan_full_matrix_and_fp32():
 
 def route(th, tw):
     mn, mx = min(th, tw), max(th, tw)
-    if mx <= 256 and mn >= 32:
+    if mx <= 256 and (mn >= 48 or (mn >= 32 and mx <= 128)):
         return "chip"
     if mx <= 64:
         return "chip-precise"

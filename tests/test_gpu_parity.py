@@ -104,10 +104,13 @@ def test_bf16_on_chip_shapes(cuda, T):
 @pytest.mark.parametrize("T", [256, 4096])
 def test_bf16_kernel_tile_256_shapes(cuda, T):
     """Tiles whose larger side is 129..256 (zero padded to 256 x 256 on chip),
-    including thin, ragged and transposed shapes."""
+    including thin, ragged and transposed shapes.  Short sides of 32..47
+    (256 x 32, 32 x 256, 171 x 40) take the fp32 step path instead, and 256 x 48
+    is the thinnest such tile on chip."""
     rng = np.random.default_rng([25, T])
     # (the shorter side <= 128 runs the narrow variant; a tall one is transposed)
     for (h, w) in [(256, 256), (256, 32), (32, 256), (200, 150), (130, 256), (256, 129), (171, 40), (97, 230),
+                   (256, 48), (48, 200),
                    (128, 256), (256, 128), (129, 128), (128, 129)]:
         x = workloads.round_to(rng.standard_normal((h, w)), "bf16")
         err, _ = full_check(x, T, "bf16")

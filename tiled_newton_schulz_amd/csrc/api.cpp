@@ -114,14 +114,17 @@ himuon_status_t check_abc(int32_t K, const float* abc) {
 // Each matrix is cut into up to four tile classes (interior T x T tiles, the
 // right-edge column, the bottom-edge row and the corner); all tiles of a class
 // share one shape, and each class is routed by that shape:
-//   bf16, both sides 32..256          -> on-chip kernel (kernel tile 32/64/128/256)
+//   bf16, both sides 48..256, or both 32..128
+//                                     -> on-chip kernel (kernel tile 32/64/128/256)
 //   bf16, a side < 32, both <= 64     -> on-chip kernel, hi/lo split precision
 //   bf16, both sides >= 64, one > 256 -> step path, bf16 workspace
 //   bf16, other thin tiles            -> step path, fp32 workspace
 //   fp32                              -> step path, fp32 workspace
-// (A bf16 iterate of a tile whose short side r is below 64 and whose long side
-// is long loses accuracy: emulated worst errors of 2.5-2.9e-2 for r = 32..40
-// and s = 600..2000 against 1.3e-2 at r = 64, with a 3e-2 bound.)
+// A bf16 iterate of a tile whose short side r is small and whose long side s
+// is long loses accuracy.  Emulated worst errors, with a 3e-2 bound:
+//   on chip:   2.6e-2 at r = 32, s = 256; 2.1e-2 at r = 32, s = 128 and at
+//              r = 48, s = 256;
+//   step path: 2.5-2.9e-2 for r = 32..40 and s = 600..2000; 1.3e-2 at r = 64.
 struct TileClass {
     int spec;                 // matrix index
     int32_t ti0, tj0, n_ti, n_tj, th, tw;
@@ -133,7 +136,7 @@ enum class Route { OnChip, OnChipPrecise, StepBf16, StepFp32 };
 Route route_of(himuon_dtype_t dt, int32_t th, int32_t tw) {
     const int32_t mn = std::min(th, tw), mx = std::max(th, tw);
     if (dt == HIMUON_FP32) return Route::StepFp32;
-    if (mx <= 256 && mn >= 32) return Route::OnChip;
+    if (mx <= 256 && (mn >= 48 || (mn >= 32 && mx <= 128))) return Route::OnChip;
     if (mx <= 64) return Route::OnChipPrecise;
     if (mn >= 64) return Route::StepBf16;
     return Route::StepFp32;
