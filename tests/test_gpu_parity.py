@@ -287,6 +287,67 @@ def test_muon_step(cuda, dt, T, shape, K):
     assert worst <= 1.0
 
 
+def check_muon(W, M, G, Wg, Mg, dt, T, K, mu, eta, tiles=None):
+    """Momentum within one rounding of mu M + G; weights within W's rounding
+    plus eta times the map's tolerance per tile (tiles: (r0, r1, c0, c1)
+    to check, default all).  Returns the worst difference / bound."""
+    mM, gG = mu * M.double(), G.double()
+    m_new = workloads.round_to((mM + gG).numpy(), dt).double()
+    bound = m_new.abs() * (2.0 ** -7 if dt == "bf16" else 2.0 ** -23) + 2.0 ** -22 * (mM.abs() + gG.abs())
+    assert bool(((Mg.cpu().double() - m_new).abs() <= bound).all()), "momentum differs beyond rounding"
+    Mh = Mg.cpu().double().numpy()
+    got = Wg.cpu().double().numpy()
+    Wd = W.double().numpy()
+    worst = 0.0
+    for r0, r1, c0, c1 in (tiles if tiles is not None else oracle.tile_grid(*Mh.shape, T)):
+        U = oracle.ns_map(Mh[r0:r1, c0:c1], COEFFS, K=K)
+        want = Wd[r0:r1, c0:c1] - eta * U
+        half_ulp = np.abs(want) * (2.0 ** -8 if dt == "bf16" else 2.0 ** -24)
+        d = np.linalg.norm(got[r0:r1, c0:c1] - want)
+        worst = max(worst, d / (np.linalg.norm(half_ulp) + eta * TOL[dt] * np.linalg.norm(U)))
+    return worst
+
+
+@pytest.mark.parametrize("shape,T", [((1100, 1030), 512), ((2100, 2100), 2100), ((1030, 2100), 2100)])
+def test_muon_step_on_step_path(cuda, shape, T):
+    """The fused Muon step where the last product writes W <- W - eta X from
+    the bf16 step GEMM: 512-tiles with edges (128 x 128 blocks) and
+    whole-matrix tiles of side 2100, whose apply runs 256 x 256 blocks (a
+    wide one, and a square one written back in place untransposed)."""
+    rng = np.random.default_rng([29, T, shape[0]])
+    W, M, G = (workloads.round_to(rng.standard_normal(shape), "bf16") for _ in range(3))
+    Wg, Mg, Gg = W.cuda(), M.cuda(), G.cuda()
+    mu, eta = 0.95, 0.02
+    H.himuon_muon_step([Wg], [Mg], [Gg], T, 5, COEFFS, mu=mu, eta=eta)
+    torch.cuda.synchronize()
+    worst = check_muon(W, M, G, Wg, Mg, "bf16", T, 5, mu, eta)
+    say(f"muon bf16 {shape} T={T}: worst difference / bound = {worst:.3f}")
+    assert worst <= 1.0
+
+
+def test_muon_step_layer_d2048(cuda):
+    """The fused Muon step on one transformer layer at d = 2048, T = 128 (the
+    Muon variant of the one-wave kernel, one workgroup per tile), with 16
+    sampled tiles per matrix checked."""
+    w = WORKLOADS["layer_d2048"]
+    Ms = workloads.host_tensors(w)
+    rng = np.random.default_rng(31)
+    Ws = [workloads.round_to(rng.standard_normal(tuple(m.shape)) * 0.02, "bf16") for m in Ms]
+    Gs = [workloads.round_to(rng.standard_normal(tuple(m.shape)), "bf16") for m in Ms]
+    Wg, Mg, Gg = [x.cuda() for x in Ws], [x.cuda() for x in Ms], [x.cuda() for x in Gs]
+    mu, eta = 0.95, 0.02
+    H.himuon_muon_step(Wg, Mg, Gg, 128, 5, COEFFS, mu=mu, eta=eta)
+    torch.cuda.synchronize()
+    worst = 0.0
+    for i in range(len(Ms)):
+        Hh, Ww = Ms[i].shape
+        tiles = [(ti * 128, min(ti * 128 + 128, Hh), tj * 128, min(tj * 128 + 128, Ww))
+                 for ti, tj in sample_tiles(Hh, Ww, 128, 16, rng)]
+        worst = max(worst, check_muon(Ws[i], Ms[i], Gs[i], Wg[i], Mg[i], "bf16", 128, 5, mu, eta, tiles))
+    say(f"muon layer_d2048 T=128: worst difference / bound = {worst:.3f}")
+    assert worst <= 1.0
+
+
 # ------------------------------------------------------------- workloads
 def test_layer_d2048(cuda):
     """One transformer layer (Q, K, V, O, MLP x3) at T = 128, one launch."""
