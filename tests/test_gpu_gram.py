@@ -81,6 +81,20 @@ def test_step_counts(cuda, dt, K):
     assert err <= TOL[dt]
 
 
+@pytest.mark.parametrize("restart", [2, 8])
+def test_max_steps(cuda, restart):
+    """K = 16 with a restart after two steps and after eight: five quintic
+    steps, then eleven cubic ones (1.5, -0.5, 0), which draw the singular
+    values to 1 (sixteen quintic steps compound bf16 rounding past 3e-2 on
+    every route, the standard map's included)."""
+    rng = np.random.default_rng([76, restart])
+    x = workloads.round_to(rng.standard_normal((300, 900)), "bf16")
+    steps = [COEFFS] * 5 + [(1.5, -0.5, 0.0)] * 11
+    err, _ = gram_check(x, "bf16", K=16, abc=steps, restart=restart)
+    say(f"gram K=16 restart={restart}: {err:.3e}")
+    assert err <= TOL["bf16"]
+
+
 def test_chunking_bit_exact(cuda):
     """A workspace that holds one matrix at a time gives the same bits as one
     chunk for all."""

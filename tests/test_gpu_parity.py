@@ -148,6 +148,25 @@ def test_step_counts_and_mixed_coefficients(cuda, dt, T, K):
     assert err <= TOL[dt]
 
 
+STEPS16 = [COEFFS] * 5 + [(1.5, -0.5, 0.0)] * 11
+
+
+@pytest.mark.parametrize("shape,T", [((300, 260), 128), ((300, 200), 256), ((600, 520), 512), ((130, 40), 64)])
+def test_max_steps(cuda, shape, T):
+    """K = 16, the largest step count, on every route (kernel tiles 128 and
+    256, the step path with bf16 and fp32 workspaces, split precision).  Five
+    quintic steps, then eleven cubic ones (1.5, -0.5, 0), which draw the
+    singular values to 1 and so damp the rounding of earlier steps: sixteen
+    quintic steps keep the singular values oscillating in a band where the
+    step polynomial's slope exceeds 1, and bf16 rounding then compounds past
+    3e-2 on every route (measured 2.4-3.5e-2)."""
+    rng = np.random.default_rng([37, T])
+    x = workloads.round_to(rng.standard_normal(shape), "bf16")
+    err, _ = full_check(x, T, "bf16", K=16, abc=STEPS16)
+    say(f"K=16 {shape} T={T}: {err:.3e}")
+    assert err <= TOL["bf16"]
+
+
 # steps with c = 0 (the cubic iteration) mixed with quintic ones
 CUBIC_MIX = [(1.5, -0.5, 0.0), (3.4445, -4.7750, 2.0315), (1.5, -0.5, 0.0), (2.0, -1.5, 0.5), (1.5, -0.5, 0.0)]
 
