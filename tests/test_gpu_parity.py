@@ -148,6 +148,36 @@ def test_step_counts_and_mixed_coefficients(cuda, dt, T, K):
     assert err <= TOL[dt]
 
 
+@pytest.mark.parametrize("eps", [0.0, 1e-3])
+def test_eps_argument(cuda, eps):
+    """eps is added to each tile's Frobenius norm: inputs scaled so that the
+    tile norms are about 1e-2, where eps = 1e-3 changes the result by about
+    10 %, on every route (kernel tiles 64, 128 and 256, the bf16 and fp32 step
+    paths, the Gram iteration)."""
+    rng = np.random.default_rng([39, int(eps * 1e4)])
+    for shape, T, dt in [((200, 150), 64, "bf16"), ((300, 260), 128, "bf16"), ((300, 200), 256, "bf16"),
+                         ((600, 520), 512, "bf16"), ((200, 150), 64, "fp32")]:
+        x = workloads.round_to(rng.standard_normal(shape) * (1e-2 / min(T, shape[0])), dt)
+        ref = oracle.tiled_ns(x.double().numpy(), T, COEFFS, eps=eps, K=5)
+        g = x.cuda()
+        H.himuon_tiled_ns([g], T, 5, COEFFS, eps=eps)
+        torch.cuda.synchronize()
+        err = oracle.tile_rel_errors(to_np(g), ref, T).max()
+        off = oracle.tile_rel_errors(oracle.tiled_ns(x.double().numpy(), T, COEFFS, eps=1e-7 if eps else 1e-3, K=5),
+                                     ref, T).max()
+        say(f"eps={eps} {dt} {shape} T={T}: {err:.3e} (the other eps is {off:.3e} away)")
+        assert err <= TOL[dt] and off > 3 * TOL[dt] * (eps > 0)
+    from oracle.gram_ns import gram_ns
+    x = workloads.round_to(rng.standard_normal((300, 900)) * (1e-2 / 300), "bf16")
+    ref = gram_ns(x.double().numpy(), [COEFFS] * 5, restart=2, eps=eps)
+    g = x.cuda()
+    H.himuon_gram_ns([g], 5, COEFFS, restart=2, eps=eps)
+    torch.cuda.synchronize()
+    err = float(np.linalg.norm(to_np(g) - ref) / np.linalg.norm(ref))
+    say(f"eps={eps} gram: {err:.3e}")
+    assert err <= TOL["bf16"]
+
+
 STEPS16 = [COEFFS] * 5 + [(1.5, -0.5, 0.0)] * 11
 
 
