@@ -374,6 +374,30 @@ def test_muon_step_on_step_path(cuda, shape, T):
     assert worst <= 1.0
 
 
+@pytest.mark.parametrize("dt,T", [("bf16", 128), ("bf16", 512), ("fp32", 64)])
+def test_muon_step_row_strides(cuda, dt, T):
+    """W, M and G with different row strides (column blocks of wider buffers,
+    at column offsets that break 16-byte alignment): the same bits as with
+    contiguous matrices."""
+    rng = np.random.default_rng([41, T])
+    shape = (600, 530)
+    W, M, G = (workloads.round_to(rng.standard_normal(shape), dt) for _ in range(3))
+    a = [W.cuda(), M.cuda(), G.cuda()]
+    H.himuon_muon_step([a[0]], [a[1]], [a[2]], T, 5, COEFFS, mu=0.9, eta=0.01)
+    bw = torch.zeros((600, 700), dtype=W.dtype, device=cuda)
+    bg = torch.zeros((600, 611), dtype=W.dtype, device=cuda)
+    Wv, Gv = bw[:, 13:13 + 530], bg[:, 3:3 + 530]
+    Wv.copy_(W.cuda())
+    Gv.copy_(G.cuda())
+    Mc = M.cuda()
+    H.himuon_muon_step([Wv], [Mc], [Gv], T, 5, COEFFS, mu=0.9, eta=0.01)
+    torch.cuda.synchronize()
+    assert torch.equal(Wv, a[0]) and torch.equal(Mc, a[1]) and torch.equal(Gv, a[2])
+    # outside the views the buffers are untouched
+    assert bw[:, :13].abs().sum().item() == 0 and bw[:, 543:].abs().sum().item() == 0
+    assert bg[:, :3].abs().sum().item() == 0 and bg[:, 533:].abs().sum().item() == 0
+
+
 def test_muon_step_layer_d2048(cuda):
     """The fused Muon step on one transformer layer at d = 2048, T = 128 (the
     Muon variant of the one-wave kernel, one workgroup per tile), with 16
