@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -408,16 +409,21 @@ MatEntry entry_of(const MatSpec& s, const TileClass& c, int64_t tile_base, int64
 struct SlotInfo {
     int slots, cus;
 };
+// Cached per device and kernel; both figures are fixed for a device, so
+// threads that race to fill an entry store the same values.
 SlotInfo slot_info(bool muon) {
-    static SlotInfo cache[2][64] = {};
+    static std::atomic<int> slots[2][64] = {};
+    static std::atomic<int> cus[2][64] = {};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return SlotInfo{0, 0};
-    SlotInfo& c = cache[muon ? 1 : 0][dev];
-    if (c.cus == 0) {
-        c.slots = resident_slots(128, muon, false);
-        c.cus = device_cus();
+    const int k = muon ? 1 : 0;
+    int c = cus[k][dev].load(std::memory_order_acquire);
+    if (c == 0) {
+        slots[k][dev].store(resident_slots(128, muon, false), std::memory_order_relaxed);
+        c = device_cus();
+        cus[k][dev].store(c, std::memory_order_release);
     }
-    return c;
+    return SlotInfo{slots[k][dev].load(std::memory_order_relaxed), c};
 }
 
 // First tile of a group's partial last round, which goes to the eight-waves-
