@@ -47,6 +47,11 @@
 #ifndef HIMUON_PERSIST128
 #define HIMUON_PERSIST128 1
 #endif
+// X' product of kernel tile 128 in units of two row blocks, each unit's
+// products interleaved with the previous unit's epilogue (0: the plain loop).
+#ifndef HIMUON_XUNITS
+#define HIMUON_XUNITS 1
+#endif
 
 namespace himuon {
 
@@ -72,6 +77,7 @@ void resident_kernel(const ResidentArgs args) {
     // I/O overlaps MFMA work instead of every wave of a round loading (and
     // storing) at the same time.
     constexpr bool PERSIST = TK == 128 && !MUON && !PRECISE && HIMUON_PERSIST128;
+    constexpr bool XUNITS = HIMUON_XUNITS;
 
     __shared__ __attribute__((aligned(16))) unsigned short sX[TK * LD];
     __shared__ __attribute__((aligned(16))) unsigned short sXl[SPLIT_X ? TK * LD : 8];
@@ -438,37 +444,92 @@ void resident_kernel(const ResidentArgs args) {
                     if constexpr (SPLIT_X) opL[buf][K][f] = tr_frag(sXl, K, J, f);
                 }
         };
-        load_ops(0, 0);
+        if constexpr (NB == 4 && XUNITS) {
+            static_assert(!MASTER32 && !SPLIT_B && !SPLIT_X, "unit pipeline: bf16 tile, one product per block");
+            // Units of work: unit u covers column block J = u / 2 and row blocks
+            // I = 2 (u % 2), 2 (u % 2) + 1 (two interleaved chains).  Unit u's
+            // products are issued together with unit u - 1's epilogue
+            // (conversion and LDS stores), the two alternating between two
+            // accumulator pairs, so that the epilogue runs under MFMAs instead
+            // of after them.  Every chain keeps its k order, so the result is
+            // that of the plain loop bit for bit.
+            f32x16 accU[2][2];
+            auto mf_unit = [&](int u) __attribute__((always_inline)) {
+                const int J = u >> 1, p = (u & 1) * 2, cur = J & 1;
+                accU[u & 1][0] = f32x16{};
+                accU[u & 1][1] = f32x16{};
 #pragma unroll
-        for (int J = 0; J < NB; ++J) {
-            const int cur = J & 1;
-            if (J + 1 < NB) load_ops(J + 1, cur ^ 1);
-            f32x16 acc[NB];
+                for (int K = 0; K < NB; ++K)
 #pragma unroll
-            for (int I = 0; I < NB; ++I) {
-                if constexpr (MASTER32) acc[I] = Xm[I][J] * ca;
-                else acc[I] = f32x16{};
-            }
+                    for (int f = 0; f < 2; ++f)
 #pragma unroll
-            for (int K = 0; K < NB; ++K)
+                        for (int i = 0; i < 2; ++i)
+                            accU[u & 1][i] = mfma32w(opA[cur][K][f], Bbf[K][p + i][f], accU[u & 1][i]);
+            };
+            auto ep_unit = [&](int u) __attribute__((always_inline)) {
+                const int J = u >> 1, p = (u & 1) * 2;
 #pragma unroll
-                for (int f = 0; f < 2; ++f)
-#pragma unroll
-                    for (int I = 0; I < NB; ++I) {
-                        acc[I] = mfma32w(opA[cur][K][f], Bbf[K][I][f], acc[I]);
-                        if constexpr (SPLIT_B) acc[I] = mfma32w(opA[cur][K][f], Blo[K][I][f], acc[I]);
-                        if constexpr (SPLIT_X) acc[I] = mfma32w(opL[cur][K][f], Bbf[K][I][f], acc[I]);
-                    }
-#pragma unroll
-            for (int I = 0; I < NB; ++I) {
-                if constexpr (MASTER32) {
-                    Xm[I][J] = acc[I];
-                } else {
-                    // column block J of X is no longer read by this step
+                for (int i = 0; i < 2; ++i)
 #pragma unroll
                     for (int m = 0; m < 4; ++m) {
-                        u32x2 v = {pack2(acc[I][4 * m], acc[I][4 * m + 1]), pack2(acc[I][4 * m + 2], acc[I][4 * m + 3])};
-                        *reinterpret_cast<u32x2*>(&sX[rl_off(I, J, m)]) = v;
+                        const f32x16& a = accU[u & 1][i];
+                        u32x2 v = {pack2(a[4 * m], a[4 * m + 1]), pack2(a[4 * m + 2], a[4 * m + 3])};
+                        *reinterpret_cast<u32x2*>(&sX[rl_off(p + i, J, m)]) = v;
+                    }
+            };
+            load_ops(0, 0);
+#pragma unroll
+            for (int u = 0; u < 2 * NB; ++u) {
+                // the operands of column block J + 1 are read with J's first unit
+                if ((u & 1) == 0 && (u >> 1) + 1 < NB) load_ops((u >> 1) + 1, ((u >> 1) + 1) & 1);
+                mf_unit(u);
+                if (u > 0) ep_unit(u - 1);
+                // 16 MFMAs, each followed by one VALU instruction, with the LDS
+                // reads of the next column block and the stores of the previous
+                // unit spread between them
+#pragma unroll
+                for (int k = 0; k < 16; ++k) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            ep_unit(2 * NB - 1);
+        } else {
+            load_ops(0, 0);
+#pragma unroll
+            for (int J = 0; J < NB; ++J) {
+                const int cur = J & 1;
+                if (J + 1 < NB) load_ops(J + 1, cur ^ 1);
+                f32x16 acc[NB];
+#pragma unroll
+                for (int I = 0; I < NB; ++I) {
+                    if constexpr (MASTER32) acc[I] = Xm[I][J] * ca;
+                    else acc[I] = f32x16{};
+                }
+#pragma unroll
+                for (int K = 0; K < NB; ++K)
+#pragma unroll
+                    for (int f = 0; f < 2; ++f)
+#pragma unroll
+                        for (int I = 0; I < NB; ++I) {
+                            acc[I] = mfma32w(opA[cur][K][f], Bbf[K][I][f], acc[I]);
+                            if constexpr (SPLIT_B) acc[I] = mfma32w(opA[cur][K][f], Blo[K][I][f], acc[I]);
+                            if constexpr (SPLIT_X) acc[I] = mfma32w(opL[cur][K][f], Bbf[K][I][f], acc[I]);
+                        }
+#pragma unroll
+                for (int I = 0; I < NB; ++I) {
+                    if constexpr (MASTER32) {
+                        Xm[I][J] = acc[I];
+                    } else {
+                        // column block J of X is no longer read by this step
+#pragma unroll
+                        for (int m = 0; m < 4; ++m) {
+                            u32x2 v = {pack2(acc[I][4 * m], acc[I][4 * m + 1]), pack2(acc[I][4 * m + 2], acc[I][4 * m + 3])};
+                            *reinterpret_cast<u32x2*>(&sX[rl_off(I, J, m)]) = v;
+                        }
                     }
                 }
             }
