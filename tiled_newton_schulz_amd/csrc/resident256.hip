@@ -12,8 +12,9 @@
 //   1. A = X X^T: the 36 lower 32x32 blocks, four or five per wave, from
 //      16-byte row fragments of X.  Each wave also copies its column block of
 //      X (32 columns) into registers, as the MFMA operand of step 3.
-//   2. A is written over X: each lower block as it is, and transposed as the
-//      upper block, so the stored A is exactly symmetric.
+//   2. A is written over X: each lower block transposed as the upper block,
+//      then read back from there with transposing reads and written as the
+//      lower block, so the stored A is exactly symmetric.
 //   3. A^2 = A A^T (A symmetric), same blocks and reads as 1; the epilogue
 //      forms B' from the same rounded A, and B' is written over A.
 //   4. X'^T(w, I) = sum_K X(K, w)^T B'(K, I): a operand = the wave's column
@@ -86,7 +87,6 @@ struct LdsLanes {
     const unsigned short* rf;   // row fragments:   (l%32) row, 8 (l/32) column
     const unsigned short* cf;   // column fragments (transposing reads)
     unsigned short* rl;         // row-layout runs:  (l%32) row, 4 (l/32) column
-    unsigned short* al;         // accumulator layout: 4 (l/32) row, (l%32) column
 };
 
 // 16-byte row fragment: row R*32 + l%32, columns k0 + 8 (l/32) .. +7.
@@ -121,11 +121,16 @@ __device__ __forceinline__ void gram_lower(const LdsLanes& L, f32x16 (&acc)[5]) 
 }
 
 // Writes the wave's lower blocks (bf16 AL in p) into the LDS matrix as a full
-// symmetric matrix: block (j, i) from the row layout (8-byte stores), block
-// (i, j) for i != j from AL (2-byte stores).
+// symmetric matrix.  Block (j, i) takes the transpose, written from the AL
+// registers as row-layout runs (8-byte stores).  For i != j, block (i, j) is
+// then read back from (j, i) column by column with transposing reads (a column
+// of the stored transpose is a row of the block) and written as 16-byte row
+// fragments.  The same bits land as with one 2-byte store per element, in a
+// quarter of the LDS instructions.
 template <int NR, int W>
 __device__ __forceinline__ void store_sym(const LdsLanes& L, const u32x4 (&p)[5][2]) {
     using B = Blocks<NR>;
+    unsigned short* wf = const_cast<unsigned short*>(L.rf);   // row-fragment positions, for writing
 #pragma unroll
     for (int b = 0; b < B::n[W]; ++b) {
         const int i = B::i[W][b], j = B::j[W][b];
@@ -134,13 +139,17 @@ __device__ __forceinline__ void store_sym(const LdsLanes& L, const u32x4 (&p)[5]
             u32x2 v = {p[b][m >> 1][2 * (m & 1)], p[b][m >> 1][2 * (m & 1) + 1]};
             *reinterpret_cast<u32x2*>(&L.rl[j * 32 * kLD + i * 32 + 8 * m]) = v;
         }
-        if (i != j) {
+    }
 #pragma unroll
-            for (int q = 0; q < 16; ++q) {
-                const unsigned word = p[b][q >> 3][(q & 7) >> 1];
-                const unsigned short v = (q & 1) ? (unsigned short)(word >> 16) : (unsigned short)(word & 0xffffu);
-                L.al[(i * 32 + (q >> 2) * 8 + (q & 3)) * kLD + j * 32] = v;
-            }
+    for (int b = 0; b < B::n[W]; ++b) {
+        const int i = B::i[W][b], j = B::j[W][b];
+        if (i != j) {
+            // lane l: row i*32 + l%32 of the block, columns 8 (l/32) .. +7 and
+            // 16 + 8 (l/32) .. +7, from column i*32 + l%32 of block (j, i)
+            const u32x4 r0 = col_frag(L, j * 32, i * 32);
+            const u32x4 r1 = col_frag(L, j * 32 + 16, i * 32);
+            *reinterpret_cast<u32x4*>(&wf[i * 32 * kLD + j * 32]) = r0;
+            *reinterpret_cast<u32x4*>(&wf[i * 32 * kLD + j * 32 + 16]) = r1;
         }
     }
 }
@@ -252,9 +261,8 @@ __global__ __launch_bounds__(512) void resident256_kernel(const ResidentArgs arg
         int o_rf = l32 * kLD + g * 8;
         int o_cf = (8 * g + ((lane & 15) >> 2)) * kLD + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
         int o_rl = l32 * kLD + 4 * g;
-        int o_al = 4 * g * kLD + l32;
-        asm volatile("" : "+v"(o_rf), "+v"(o_cf), "+v"(o_rl), "+v"(o_al));
-        const LdsLanes L{sX + o_rf, sX + o_cf, sX + o_rl, sX + o_al};
+        asm volatile("" : "+v"(o_rf), "+v"(o_cf), "+v"(o_rl));
+        const LdsLanes L{sX + o_rf, sX + o_cf, sX + o_rl};
         f32x16 acc[5];
         u32x4 p[5][2];
         // 1. lower blocks of A = X X^T (k over the 256 columns); this wave's
