@@ -7,7 +7,7 @@
 // (Algorithm 1): A = X X^T, B = b A + c A^2, X <- a X + B X.  Padding is exact:
 // the padded Gram matrix is block diagonal, so padded rows and columns stay 0.
 //
-// The LDS (160 KB) holds one 256 x 256 bf16 matrix at a time (132 KB with
+// The LDS (160 KB) holds one 256 x 256 bf16 matrix at a time (140 KB with
 // row padding), in turn X, A and B' = a I + b A + c A^2:
 //   1. A = X X^T: the 36 lower 32x32 blocks, four or five per wave, from
 //      16-byte row fragments of X.  Each wave also copies its column block of
@@ -40,7 +40,9 @@ namespace himuon {
 
 namespace {
 
-constexpr int kT = 256, kLD = kT + 8;
+// LDS row stride: 280 elements (560 bytes).  Measured against 264 (1-2 % slower
+// on every T = 256 workload), 272 (5 % slower), 296 and 312 (level).
+constexpr int kT = 256, kLD = kT + 24;
 
 // Lower 32x32 blocks (i, j), i >= j, of a symmetric product with NR x NR
 // blocks, per wave (at most five).
