@@ -39,6 +39,7 @@
 //    products per contraction (the lo x lo term dropped).
 
 #include <atomic>
+#include <type_traits>
 
 #include "device_util.h"
 
@@ -51,6 +52,9 @@
 // products interleaved with the previous unit's epilogue (0: the plain loop).
 #ifndef HIMUON_XUNITS
 #define HIMUON_XUNITS 1
+#endif
+#ifndef HIMUON_FOLD
+#define HIMUON_FOLD 1
 #endif
 
 namespace himuon {
@@ -78,6 +82,14 @@ void resident_kernel(const ResidentArgs args) {
     // storing) at the same time.
     constexpr bool PERSIST = TK == 128 && !MUON && !PRECISE && HIMUON_PERSIST128;
     constexpr bool XUNITS = HIMUON_XUNITS;
+    // Kernel tile 128 folds the normalisation into the first step (K > 0):
+    // the raw tile goes to LDS, the sum of squares is taken from the row
+    // fragments of the first A product, and that step rounds s^2 A (the A of
+    // the scaled tile) and scales the coefficients of B' by s, so that it
+    // applies s B'(s^2 A) to the raw tile.  The eight-wave kernel does the
+    // same, operation for operation.
+    constexpr bool FOLD = TK == 128 && HIMUON_FOLD;
+    using FIRSTC = std::bool_constant<FOLD>;
 
     __shared__ __attribute__((aligned(16))) unsigned short sX[TK * LD];
     __shared__ __attribute__((aligned(16))) unsigned short sXl[SPLIT_X ? TK * LD : 8];
@@ -137,13 +149,18 @@ void resident_kernel(const ResidentArgs args) {
                 chunk[it] = v;
             }
         }
+        if (!FOLD || args.K == 0) {
 #pragma unroll
-        for (int it = 0; it < IO::NCH; ++it)
+            for (int it = 0; it < IO::NCH; ++it)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) { float x = bf2f(chunk[it][e]); ss = __builtin_fmaf(x, x, ss); }
+                for (int e = 0; e < 8; ++e) { float x = bf2f(chunk[it][e]); ss = __builtin_fmaf(x, x, ss); }
+        }
     }
-    ss = wave_sum(ss);
-    const float scale = args.normalize ? 1.0f / (sqrtf(ss) + args.eps) : 1.0f;
+    float scale = 1.0f;
+    if (!FOLD || args.K == 0) {
+        ss = wave_sum(ss);
+        scale = args.normalize ? 1.0f / (sqrtf(ss) + args.eps) : 1.0f;
+    }
 
     // RL run (block I,J; run m = q/4): row I*32 + l32, cols J*32 + 8m + 4g .. +3
     auto rl_off = [&](int I, int J, int m) { return (I * 32 + l32) * LD + J * 32 + 8 * m + 4 * g; };
@@ -204,6 +221,14 @@ void resident_kernel(const ResidentArgs args) {
                     for (int e = 0; e < 4; ++e) Xm[I][J][4 * m + e] = bf2f(v[e]) * scale;
                 }
         __syncthreads();
+    } else if (FOLD && args.K > 0) {
+#pragma unroll
+        for (int it = 0; it < IO::NCH; ++it) {
+            const int idx = it * 64 + lane;
+            const int r = idx / IO::CPR, col = (idx % IO::CPR) * 8;
+            *reinterpret_cast<u16x8*>(&sX[r * LD + col]) = chunk[it];
+        }
+        __syncthreads();
     } else {
 #pragma unroll
         for (int it = 0; it < IO::NCH; ++it) {
@@ -221,8 +246,12 @@ void resident_kernel(const ResidentArgs args) {
     const int tn = t + (int)gridDim.x;
     const bool next = PERSIST && tn < args.tile_end;
     // before_apply runs between B' and the X' product (the prefetch hook)
-    auto ns_step = [&](int step, auto before_apply) __attribute__((always_inline)) {
-        const float ca = args.abc[3 * step], cb = args.abc[3 * step + 1], cc = args.abc[3 * step + 2];
+    // first: the first step of a folded tile (raw tile in LDS)
+    auto ns_step = [&](int step, auto before_apply, auto first) __attribute__((always_inline)) {
+        constexpr bool FIRST = decltype(first)::value;
+        static_assert(!FIRST || (FOLD && SYM), "folded normalisation: kernel tile 128");
+        float ca = args.abc[3 * step], cb = args.abc[3 * step + 1], cc = args.abc[3 * step + 2];
+        float s2 = 1.0f;   // scale of A in the first folded step
         u32x4 Abf[NB][NB][2];                       // AL(A), bf16 (hi)
         u32x4 Alo[SPLIT_A ? NB : 1][SPLIT_A ? NB : 1][2];
         u32x4 Bbf[NB][NB][2];                       // AL(B)
@@ -284,6 +313,26 @@ void resident_kernel(const ResidentArgs args) {
 #pragma unroll
                 for (int kc = 0; kc < NK; ++kc)
                     RF[I][kc] = *reinterpret_cast<const u32x4*>(&sX[(I * 32 + l32) * LD + kc * 16 + g * 8]);
+            if constexpr (FIRST) {
+                // sum of squares of the raw tile, in row-fragment order
+                float sq = 0.f;
+#pragma unroll
+                for (int I = 0; I < NB; ++I)
+#pragma unroll
+                    for (int kc = 0; kc < NK; ++kc)
+#pragma unroll
+                        for (int k = 0; k < 4; ++k) {
+                            const float x0 = lo_f(RF[I][kc][k]), x1 = hi_f(RF[I][kc][k]);
+                            sq = __builtin_fmaf(x0, x0, sq);
+                            sq = __builtin_fmaf(x1, x1, sq);
+                        }
+                sq = wave_sum(sq);
+                const float sc = args.normalize ? 1.0f / (sqrtf(sq) + args.eps) : 1.0f;
+                s2 = sc * sc;
+                ca *= sc;
+                cb *= sc;
+                cc *= sc;
+            }
             // lower blocks (I >= J), two accumulator chains at a time
             constexpr int NL = NB * (NB + 1) / 2;
 #pragma unroll
@@ -306,6 +355,10 @@ void resident_kernel(const ResidentArgs args) {
                 for (int kc = 0; kc < NK; ++kc) {
                     a1 = mfma32w(RF[I1][kc], RF[J1][kc], a1);
                     if (two) a2 = mfma32w(RF[I2][kc], RF[J2][kc], a2);
+                }
+                if constexpr (FIRST) {
+                    a1 = a1 * s2;
+                    a2 = a2 * s2;
                 }
                 Abf[I1][J1][0] = cvt8(a1, 0); Abf[I1][J1][1] = cvt8(a1, 8);
                 if (two) { Abf[I2][J2][0] = cvt8(a2, 0); Abf[I2][J2][1] = cvt8(a2, 8); }
@@ -565,11 +618,21 @@ void resident_kernel(const ResidentArgs args) {
         for (int it = 0; it < IO::NCH; ++it) chunk[it] = u16x8{};
     };
     if constexpr (PERSIST) {
-        for (int step = 0; step < args.K - 1; ++step) ns_step(step, no_hook);
-        if (args.K > 0) ns_step(args.K - 1, prefetch);
-        else prefetch(0u);
+        static_assert(FOLD || !HIMUON_FOLD, "the grid-stride kernel is kernel tile 128");
+        if (args.K >= 2) {
+            ns_step(0, no_hook, FIRSTC{});
+            for (int step = 1; step < args.K - 1; ++step) ns_step(step, no_hook, std::false_type{});
+            ns_step(args.K - 1, prefetch, std::false_type{});
+        } else if (args.K == 1) {
+            ns_step(0, prefetch, FIRSTC{});
+        } else {
+            prefetch(0u);
+        }
+    } else if constexpr (FOLD) {
+        if (args.K > 0) ns_step(0, no_hook, FIRSTC{});
+        for (int step = 1; step < args.K; ++step) ns_step(step, no_hook, std::false_type{});
     } else {
-        for (int step = 0; step < args.K; ++step) ns_step(step, no_hook);
+        for (int step = 0; step < args.K; ++step) ns_step(step, no_hook, std::false_type{});
     }
 
     // ---- write back in place (Muon: W <- W - eta X) ----
@@ -677,32 +740,53 @@ __global__ __launch_bounds__(512) void resident_coop_kernel(const ResidentArgs a
         }
     }
     __syncthreads();
-    // sum of squares in the one-wave kernel's order (lane l sums chunks l, l + 64, ...)
+    // Sum of squares in the one-wave kernel's order.  With K > 0 the
+    // normalisation is folded into the first step there (row-fragment order:
+    // lane l sums rows l % 32 + 32 I, columns 16 kc + 8 (l / 32) .. + 7); with
+    // K = 0 it is taken at load (lane l sums chunks l, l + 64, ...).
+    const bool fold = HIMUON_FOLD && args.K > 0;
     if (w == 0) {
         float ss = 0.f;
+        if (fold) {
 #pragma unroll
-        for (int it = 0; it < IO::NCH; ++it) {
-            const int idx = it * 64 + lane;
-            const int r = idx / IO::CPR, col = (idx % IO::CPR) * 8;
-            const u16x8 v = *reinterpret_cast<const u16x8*>(&sX[r * LD + col]);
+            for (int I = 0; I < NB; ++I)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) { float x = bf2f(v[e]); ss = __builtin_fmaf(x, x, ss); }
+                for (int kc = 0; kc < NK; ++kc) {
+                    const u32x4 v = *reinterpret_cast<const u32x4*>(&sX[(I * 32 + l32) * LD + kc * 16 + g * 8]);
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const float x0 = lo_f(v[k]), x1 = hi_f(v[k]);
+                        ss = __builtin_fmaf(x0, x0, ss);
+                        ss = __builtin_fmaf(x1, x1, ss);
+                    }
+                }
+        } else {
+#pragma unroll
+            for (int it = 0; it < IO::NCH; ++it) {
+                const int idx = it * 64 + lane;
+                const int r = idx / IO::CPR, col = (idx % IO::CPR) * 8;
+                const u16x8 v = *reinterpret_cast<const u16x8*>(&sX[r * LD + col]);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) { float x = bf2f(v[e]); ss = __builtin_fmaf(x, x, ss); }
+            }
         }
         ss = wave_sum(ss);
         if (lane == 0) red[0] = ss;
     }
     __syncthreads();
     const float scale = args.normalize ? 1.0f / (sqrtf(red[0]) + args.eps) : 1.0f;
+    if (!fold) {
 #pragma unroll
-    for (int it = 0; it < NCH; ++it) {
-        const int idx = it * 512 + tid;
-        const int r = idx / IO::CPR, col = (idx % IO::CPR) * 8;
-        u16x8 v;
+        for (int it = 0; it < NCH; ++it) {
+            const int idx = it * 512 + tid;
+            const int r = idx / IO::CPR, col = (idx % IO::CPR) * 8;
+            u16x8 v;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = f2bf(bf2f(chunk[it][e]) * scale);
-        *reinterpret_cast<u16x8*>(&sX[r * LD + col]) = v;
+            for (int e = 0; e < 8; ++e) v[e] = f2bf(bf2f(chunk[it][e]) * scale);
+            *reinterpret_cast<u16x8*>(&sX[r * LD + col]) = v;
+        }
+        __syncthreads();
     }
-    __syncthreads();
 
     auto frag = [&](int K, int P, int f) -> u32x4& { return sF[((K * NB + P) * 2 + f) * 64 + lane]; };
     auto tr_frag = [&](int K, int J, int f) {
@@ -715,7 +799,15 @@ __global__ __launch_bounds__(512) void resident_coop_kernel(const ResidentArgs a
     };
 
     for (int step = 0; step < args.K; ++step) {
-        const float ca = args.abc[3 * step], cb = args.abc[3 * step + 1], cc = args.abc[3 * step + 2];
+        float ca = args.abc[3 * step], cb = args.abc[3 * step + 1], cc = args.abc[3 * step + 2];
+        // the first folded step: A of the scaled tile is s^2 A, and B' is scaled by s
+        const bool first = fold && step == 0;
+        const float s2 = scale * scale;
+        if (first) {
+            ca *= scale;
+            cb *= scale;
+            cc *= scale;
+        }
         u32x4 Aown[2][2];   // AL(A(2h + i, c))
         u32x4 Bown[2][2];   // AL(B'(2h + i, c))
         {
@@ -732,6 +824,7 @@ __global__ __launch_bounds__(512) void resident_coop_kernel(const ResidentArgs a
             }
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
+                if (first) acc[i] = acc[i] * s2;
                 Aown[i][0] = cvt8(acc[i], 0);
                 Aown[i][1] = cvt8(acc[i], 8);
                 frag(2 * h + i, c, 0) = Aown[i][0];
