@@ -606,6 +606,30 @@ def test_dense8192_schedule(cuda):
     assert worst <= TOL["bf16"]
 
 
+# ------------------------------------------------------------- input scale
+@pytest.mark.parametrize("scale_exp", [50, -50])
+def test_scale_extremes_tile128(cuda, scale_exp):
+    """Inputs scaled by 2^50 and 2^-50 (exact in bf16) at T = 128, where the
+    normalisation is folded into the first step (s^2 A formed from the fp32
+    X X^T of the raw tile): a batch that goes to the eight-wave kernel (15
+    tiles, ragged edges) and one that goes to the one-wave kernel (600 tiles).
+    Every tile against the oracle, which normalises in fp64."""
+    rng = np.random.default_rng([97, scale_exp + 100])
+    f = 2.0 ** scale_exp
+    small = [workloads.round_to(rng.standard_normal((300, 520)) * f, "bf16")]
+    big = [workloads.round_to(rng.standard_normal((640, 640)) * f, "bf16") for _ in range(24)]
+    for name, hosts in (("15 tiles", small), ("600 tiles", big)):
+        devs = [x.cuda() for x in hosts]
+        H.himuon_tiled_ns(devs, 128, 5, COEFFS)
+        torch.cuda.synchronize()
+        worst = 0.0
+        for x, d in zip(hosts, devs):
+            ref = oracle.tiled_ns(x.double().numpy(), 128, COEFFS, K=5)
+            worst = max(worst, float(oracle.tile_rel_errors(to_np(d), ref, 128).max()))
+        say(f"scale 2^{scale_exp}, {name}: worst per-tile error {worst:.3e}")
+        assert worst <= TOL["bf16"]
+
+
 # ------------------------------------------------------------- error tails
 @pytest.mark.parametrize("T,N", [(32, 48), (64, 48), (128, 24)])
 def test_error_tail_over_many_tiles(cuda, T, N):
