@@ -611,9 +611,10 @@ def test_dense8192_schedule(cuda):
 def test_scale_extremes_tile128(cuda, scale_exp):
     """Inputs scaled by 2^50 and 2^-50 (exact in bf16) at T = 128, where the
     normalisation is folded into the first step (s^2 A formed from the fp32
-    X X^T of the raw tile): a batch that goes to the eight-wave kernel (15
-    tiles, ragged edges) and one that goes to the one-wave kernel (600 tiles).
-    Every tile against the oracle, which normalises in fp64."""
+    X X^T of the raw tile): one 300 x 520 matrix (15 tiles; its full tiles
+    and 44 x 128 edge tiles form a partial round for the eight-wave kernel, its
+    8-column edge tiles take other paths) and 600 full tiles on the one-wave
+    kernel.  Every tile against the oracle, which normalises in fp64."""
     rng = np.random.default_rng([97, scale_exp + 100])
     f = 2.0 ** scale_exp
     small = [workloads.round_to(rng.standard_normal((300, 520)) * f, "bf16")]
