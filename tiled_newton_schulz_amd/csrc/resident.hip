@@ -741,26 +741,15 @@ __global__ __launch_bounds__(512) void resident_coop_kernel(const ResidentArgs a
     }
     __syncthreads();
     // Sum of squares in the one-wave kernel's order.  With K > 0 the
-    // normalisation is folded into the first step there (row-fragment order:
-    // lane l sums rows l % 32 + 32 I, columns 16 kc + 8 (l / 32) .. + 7); with
-    // K = 0 it is taken at load (lane l sums chunks l, l + 64, ...).
+    // normalisation is folded into the first step there: the sum is taken in
+    // row-fragment order (lane l sums rows l % 32 + 32 I, columns
+    // 16 kc + 8 (l / 32) .. + 7) once the first step's A products are issued.
+    // With K = 0 it is taken here (lane l sums chunks l, l + 64, ...).
     const bool fold = HIMUON_FOLD && args.K > 0;
-    if (w == 0) {
-        float ss = 0.f;
-        if (fold) {
-#pragma unroll
-            for (int I = 0; I < NB; ++I)
-#pragma unroll
-                for (int kc = 0; kc < NK; ++kc) {
-                    const u32x4 v = *reinterpret_cast<const u32x4*>(&sX[(I * 32 + l32) * LD + kc * 16 + g * 8]);
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        const float x0 = lo_f(v[k]), x1 = hi_f(v[k]);
-                        ss = __builtin_fmaf(x0, x0, ss);
-                        ss = __builtin_fmaf(x1, x1, ss);
-                    }
-                }
-        } else {
+    float scale = 1.0f;
+    if (!fold) {
+        if (w == 0) {
+            float ss = 0.f;
 #pragma unroll
             for (int it = 0; it < IO::NCH; ++it) {
                 const int idx = it * 64 + lane;
@@ -769,13 +758,11 @@ __global__ __launch_bounds__(512) void resident_coop_kernel(const ResidentArgs a
 #pragma unroll
                 for (int e = 0; e < 8; ++e) { float x = bf2f(v[e]); ss = __builtin_fmaf(x, x, ss); }
             }
+            ss = wave_sum(ss);
+            if (lane == 0) red[0] = ss;
         }
-        ss = wave_sum(ss);
-        if (lane == 0) red[0] = ss;
-    }
-    __syncthreads();
-    const float scale = args.normalize ? 1.0f / (sqrtf(red[0]) + args.eps) : 1.0f;
-    if (!fold) {
+        __syncthreads();
+        scale = args.normalize ? 1.0f / (sqrtf(red[0]) + args.eps) : 1.0f;
 #pragma unroll
         for (int it = 0; it < NCH; ++it) {
             const int idx = it * 512 + tid;
@@ -802,12 +789,6 @@ __global__ __launch_bounds__(512) void resident_coop_kernel(const ResidentArgs a
         float ca = args.abc[3 * step], cb = args.abc[3 * step + 1], cc = args.abc[3 * step + 2];
         // the first folded step: A of the scaled tile is s^2 A, and B' is scaled by s
         const bool first = fold && step == 0;
-        const float s2 = scale * scale;
-        if (first) {
-            ca *= scale;
-            cb *= scale;
-            cc *= scale;
-        }
         u32x4 Aown[2][2];   // AL(A(2h + i, c))
         u32x4 Bown[2][2];   // AL(B'(2h + i, c))
         {
@@ -822,9 +803,36 @@ __global__ __launch_bounds__(512) void resident_coop_kernel(const ResidentArgs a
                     acc[i] = mfma32w(ri, rc, acc[i]);
                 }
             }
+            if (first) {
+                if (w == 0) {
+                    float ss = 0.f;
+#pragma unroll
+                    for (int I = 0; I < NB; ++I)
+#pragma unroll
+                        for (int kc = 0; kc < NK; ++kc) {
+                            const u32x4 v =
+                                *reinterpret_cast<const u32x4*>(&sX[(I * 32 + l32) * LD + kc * 16 + g * 8]);
+#pragma unroll
+                            for (int k = 0; k < 4; ++k) {
+                                const float x0 = lo_f(v[k]), x1 = hi_f(v[k]);
+                                ss = __builtin_fmaf(x0, x0, ss);
+                                ss = __builtin_fmaf(x1, x1, ss);
+                            }
+                        }
+                    ss = wave_sum(ss);
+                    if (lane == 0) red[0] = ss;
+                }
+                __syncthreads();
+                scale = args.normalize ? 1.0f / (sqrtf(red[0]) + args.eps) : 1.0f;
+                const float s2 = scale * scale;
+                ca *= scale;
+                cb *= scale;
+                cc *= scale;
+#pragma unroll
+                for (int i = 0; i < 2; ++i) acc[i] = acc[i] * s2;
+            }
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
-                if (first) acc[i] = acc[i] * s2;
                 Aown[i][0] = cvt8(acc[i], 0);
                 Aown[i][1] = cvt8(acc[i], 8);
                 frag(2 * h + i, c, 0) = Aown[i][0];
