@@ -537,6 +537,30 @@ def test_tail_split_bit_exact(cuda):
         assert torch.equal(single, m)
 
 
+@pytest.mark.parametrize("K", [1, 2, 3])
+def test_grid_stride_small_k_bit_exact(cuda, K):
+    """K = 1, 2 and 3 on the grid-stride launch, where the folded first step is
+    also the last one (K = 1, which then issues the next tile's loads) or comes
+    right before it.  1,875 tiles of 128 in one call run one wave per tile;
+    matrix-by-matrix calls (at most 256 tiles each) run eight waves per tile
+    with the same arithmetic, so the two agree bit for bit.  Sampled tiles,
+    edges included, against the oracle."""
+    rng = np.random.default_rng([44, K])
+    shapes = [(2048, 2048), (1000, 1500), (2048, 2048), (300, 2100), (2048, 2048), (2048, 700),
+              (2048, 2048), (1500, 1000), (2048, 2048), (2048, 2048)]
+    base = [workloads.round_to(rng.standard_normal(s), "bf16").cuda() for s in shapes]
+    abc = MIXED[:K]
+    picks = grab(base, 128, 6, rng)
+    batched = [b.clone() for b in base]
+    run(batched, 128, K=K, abc=abc)
+    worst = check_sampled(picks, batched, 128, abc, K, TOL["bf16"])
+    say(f"K={K}: worst sampled tile error {worst:.3e}")
+    for i, (b, m) in enumerate(zip(base, batched)):
+        single = b.clone()
+        run([single], 128, K=K, abc=abc)
+        assert torch.equal(single, m), i
+
+
 def test_grid_stride_ragged_mix_bit_exact(cuda):
     """More kernel-tile-128 tiles than the device holds at once (1,875), full
     and ragged tile classes mixed: each workgroup then walks several tiles,
