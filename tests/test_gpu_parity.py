@@ -561,6 +561,26 @@ def test_grid_stride_small_k_bit_exact(cuda, K):
         assert torch.equal(single, m), i
 
 
+def test_muon_tail_split_bit_exact(cuda):
+    """The fused Muon step on one layer (3,136 tiles: 3,072 one-wave, the last 64
+    eight-wave) against matrix-by-matrix Muon steps, which split the tiles
+    between the two kernels differently (a 2048 x 2048 matrix alone is a partial
+    round, all eight-wave; the last matrix's final 64 tiles run one-wave): W and
+    M equal bit for bit."""
+    w = WORKLOADS["layer_d2048"]
+    rng = np.random.default_rng([45, 1])
+    Ms = [t.cuda() for t in workloads.host_tensors(w)]
+    Gs = [workloads.round_to(rng.standard_normal(tuple(m.shape)), "bf16").cuda() for m in Ms]
+    Ws = [workloads.round_to(rng.standard_normal(tuple(m.shape)), "bf16").cuda() for m in Ms]
+    Wb, Mb = [x.clone() for x in Ws], [x.clone() for x in Ms]
+    H.himuon_muon_step(Wb, Mb, Gs, 128, 5, COEFFS, mu=0.9, eta=0.02)
+    for i in range(len(Ms)):
+        W1, M1 = Ws[i].clone(), Ms[i].clone()
+        H.himuon_muon_step([W1], [M1], [Gs[i]], 128, 5, COEFFS, mu=0.9, eta=0.02)
+        torch.cuda.synchronize()
+        assert torch.equal(M1, Mb[i]) and torch.equal(W1, Wb[i]), i
+
+
 def test_grid_stride_ragged_mix_bit_exact(cuda):
     """More kernel-tile-128 tiles than the device holds at once (1,875), full
     and ragged tile classes mixed: each workgroup then walks several tiles,
