@@ -33,7 +33,8 @@
 //  * kernel tiles 64 and 128 keep the tile in LDS as bf16, compute only the
 //    lower blocks of A and A^2, and fold a X into the product,
 //    X' = (a I + B) X, equal in exact arithmetic, with a added to the diagonal
-//    of B before it is rounded.
+//    of B before it is rounded.  Kernel tile 128 keeps the raw tile and folds
+//    the normalisation into the first step (s^2 A rounded, a, b, c times s).
 //  * PRECISE (tiles with a side below 32, where bf16 rounding of a small
 //    Gram matrix dominates): X, A and B all carried as bf16 hi/lo pairs, three
 //    products per contraction (the lo x lo term dropped).
@@ -715,7 +716,8 @@ __global__ __launch_bounds__(512) void resident_coop_kernel(const ResidentArgs a
     using IO = TileIO<TK>;
     constexpr int NCH = TK * IO::CPR / 512;   // 16-byte chunks per thread
 
-    // ---- load (Muon: M <- mu M + G, stored), sum of squares, normalise ----
+    // ---- load (Muon: M <- mu M + G, stored) into LDS; with K = 0 the sum of
+    //      squares and the scaling here, with K > 0 folded into the first step ----
     u16x8 chunk[NCH];
     {
         const unsigned short* gbase = nullptr;
