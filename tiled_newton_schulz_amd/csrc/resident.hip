@@ -54,6 +54,8 @@
 #ifndef HIMUON_XUNITS
 #define HIMUON_XUNITS 1
 #endif
+// Kernel tile 128 (one-wave and eight-wave kernels alike) folds the tile's
+// normalisation into its first step (0: a separate scaling pass).
 #ifndef HIMUON_FOLD
 #define HIMUON_FOLD 1
 #endif
