@@ -246,6 +246,83 @@ def test_schedule_block_diagonal_locality():
         tiled_ns_schedule(X, [32, 64], MIXED[:2])
 
 
+def _svd_step_schedule(X, Ts, coeffs, eps=EPS_DEFAULT):
+    """The schedule built another way: normalise every Ts[0]-tile, then for
+    step t replace every Ts[t]-tile by U p_t(S) V^T from its own SVD (the SVD
+    view of one Newton-Schulz step on the Gram Newton-Schulz page, section 3)."""
+    X = np.array(X, dtype=np.float64, copy=True)
+    H, W = X.shape
+    T0 = Ts[0]
+    for r0 in range(0, H, T0):
+        for c0 in range(0, W, T0):
+            blk = X[r0:r0 + T0, c0:c0 + T0]
+            X[r0:r0 + T0, c0:c0 + T0] = blk / (np.linalg.norm(blk) + eps)
+    for (a, b, c), T in zip(coeffs, Ts):
+        for r0 in range(0, H, T):
+            for c0 in range(0, W, T):
+                U, S, Vt = np.linalg.svd(X[r0:r0 + T, c0:c0 + T], full_matrices=False)
+                X[r0:r0 + T, c0:c0 + T] = (U * (a * S + b * S ** 3 + c * S ** 5)) @ Vt
+    return X
+
+
+@pytest.mark.parametrize("shape,Ts", [((150, 200), [64, 32, 32]), ((128, 192), [128, 64, 32, 32]),
+                                       ((96, 96), [96, 48, 16, 16])])
+def test_schedule_per_step_svd(shape, Ts):
+    """Step t of the schedule acts on the Ts[t]-tiles of the current iterate:
+    a generic (not block-diagonal) input, against the per-step SVD form."""
+    X = rng(18).standard_normal(shape)
+    got = tiled_ns_schedule(X, Ts, MIXED[:len(Ts)])
+    want = _svd_step_schedule(X, Ts, MIXED[:len(Ts)])
+    assert np.linalg.norm(got - want) <= 1e-11 * np.linalg.norm(want)
+    # the input tells the sizes apart: the first size held for every step
+    # gives a visibly different result
+    coarse = _svd_step_schedule(X, [Ts[0]] * len(Ts), MIXED[:len(Ts)])
+    assert np.linalg.norm(coarse - want) > 1e-2 * np.linalg.norm(want)
+
+
+def test_schedule_rank_one_closed_form():
+    """A rank-one 64-tile u v^T under the schedule 64 -> 32 (eps = 0).  After
+    the coarse step the tile is p1(1) u v^T / (|u| |v|), so its 32-subtile
+    (i, j) is rank one with singular value s_ij = p1(1) |u_i| |v_j| / (|u| |v|),
+    and the fine step scales it by p2(s_ij) / s_ij."""
+    r = rng(19)
+    u, v = r.standard_normal(64), r.standard_normal(64)
+    u[:32] *= 3.0   # unequal halves: the four subtiles get different s_ij
+    v[32:] *= 0.25
+    X = np.outer(u, v)
+    c1, c2 = MIXED[0], MIXED[1]
+    got = tiled_ns_schedule(X, [64, 32], [c1, c2], eps=0.0)
+    p1 = scalar_poly(1.0, [c1])
+    nu, nv = np.linalg.norm(u), np.linalg.norm(v)
+    for i in (0, 32):
+        for j in (0, 32):
+            ui, vj = u[i:i + 32], v[j:j + 32]
+            s = p1 * np.linalg.norm(ui) * np.linalg.norm(vj) / (nu * nv)
+            want = scalar_poly(s, [c2]) / s * (p1 / (nu * nv)) * np.outer(ui, vj)
+            np.testing.assert_allclose(got[i:i + 32, j:j + 32], want, rtol=0,
+                                       atol=1e-13 * np.abs(want).max())
+
+
+def test_muon_step_rank_one_closed_form():
+    """M = u v^T, G = u w^T: the new momentum is u (mu v + w)^T, rank one, so
+    with eps = 0 every T-tile (i, j) of the update is p(1) u_i z_j^T /
+    (|u_i| |z_j|) with z = mu v + w; W moves by -eta times that."""
+    r = rng(20)
+    u, v, w = r.standard_normal(64), r.standard_normal(96), r.standard_normal(96)
+    W0 = r.standard_normal((64, 96))
+    mu, eta, T = 0.9, 0.05, 32
+    Wn, Mn = muon_step(W0, np.outer(u, v), np.outer(u, w), mu=mu, eta=eta, T=T, coeffs=MIXED, eps=0.0)
+    z = mu * v + w
+    np.testing.assert_allclose(Mn, np.outer(u, z), rtol=0, atol=1e-13)
+    p = scalar_poly(1.0, MIXED)
+    for r0 in range(0, 64, T):
+        for c0 in range(0, 96, T):
+            ui, zj = u[r0:r0 + T], z[c0:c0 + T]
+            upd = p * np.outer(ui, zj) / (np.linalg.norm(ui) * np.linalg.norm(zj))
+            np.testing.assert_allclose(Wn[r0:r0 + T, c0:c0 + T], W0[r0:r0 + T, c0:c0 + T] - eta * upd,
+                                       rtol=0, atol=1e-13)
+
+
 def test_muon_step_composition():
     r = rng(17)
     W, M, G = (r.standard_normal((64, 96)) for _ in range(3))
