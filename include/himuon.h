@@ -24,7 +24,8 @@
  *   element size; no other alignment is required (16-byte aligned rows take a
  *   vector fast path).
  * - The caller owns all device memory.  The library allocates no device memory
- *   and keeps no device state between calls.  The descriptor array and the
+ *   and keeps no device state between calls (himuon_tiled_ns_noalloc aside,
+ *   which uses a fixed scratch array the library holds on each device).  The descriptor array and the
  *   coefficient array are read during the call only.  A call issues kernel
  *   launches only (no memsets or copies), so it may be captured in a HIP graph,
  *   and calls on different streams may run at once on disjoint matrices and
@@ -141,6 +142,33 @@ himuon_status_t himuon_workspace_size(const himuon_matrix_t* m, int32_t n, int32
 himuon_status_t himuon_tiled_ns(const himuon_matrix_t* m, int32_t n, int32_t T, int32_t K,
                                 const float* abc, himuon_dtype_t dt, float eps,
                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device scratch the library holds for himuon_tiled_ns_noalloc. */
+#define HIMUON_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+
+/*
+ * himuon_tiled_ns_noalloc - himuon_tiled_ns for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, and
+ * harnesses that forbid hipMalloc.  It computes exactly what himuon_tiled_ns
+ * computes (same kernels, same per-tile arithmetic, so the same bits) and
+ * allocates nothing: the step-by-step path runs through a fixed scratch array
+ * of HIMUON_NOALLOC_SCRATCH_BYTES (128 MiB) that the library holds on every
+ * device it runs on, from the first use there until the process ends.  Tiles
+ * are processed in chunks that fit it.
+ *
+ * Arguments as for himuon_tiled_ns, without the workspace.
+ * Errors: as for himuon_tiled_ns; HIMUON_ERR_WORKSPACE when one tile of the
+ * step-by-step path needs more than HIMUON_NOALLOC_SCRATCH_BYTES on its own
+ * (for example a full-matrix map above about 64 M bf16 elements), reported
+ * before the device is touched; HIMUON_ERR_HIP if the scratch address cannot
+ * be obtained on the current device.
+ * Every call on one device shares that device's scratch, which keeps the last
+ * call's contents (nothing in it needs to start at zero).  Calls whose work
+ * overlaps in time on one device (other streams, other threads) race on it:
+ * order them on one stream, or use himuon_tiled_ns with separate workspaces.
+ */
+himuon_status_t himuon_tiled_ns_noalloc(const himuon_matrix_t* m, int32_t n, int32_t T, int32_t K,
+                                        const float* abc, himuon_dtype_t dt, float eps, void* stream);
 
 /*
  * himuon_tiled_ns_schedule - K Newton-Schulz steps with a tile size per step:

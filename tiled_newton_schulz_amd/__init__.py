@@ -20,7 +20,9 @@ MAX_STEPS = 16
 
 STATUS = {0: "HIMUON_OK", 1: "HIMUON_ERR_INVALID_ARGUMENT", 2: "HIMUON_ERR_UNSUPPORTED",
           3: "HIMUON_ERR_LAYOUT", 4: "HIMUON_ERR_OVERLAP", 5: "HIMUON_ERR_WORKSPACE", 6: "HIMUON_ERR_HIP"}
-EXPORTS = ["himuon_plan", "himuon_workspace_size", "himuon_tiled_ns", "himuon_tiled_ns_schedule",
+NOALLOC_SCRATCH_BYTES = 128 << 20
+EXPORTS = ["himuon_plan", "himuon_workspace_size", "himuon_tiled_ns", "himuon_tiled_ns_noalloc",
+           "himuon_tiled_ns_schedule",
            "himuon_muon_step", "himuon_gram_ns", "himuon_gram_ns_workspace", "himuon_pair_stats",
            "himuon_pair_stats_workspace", "himuon_status_string",
            "himuon_last_hip_error", "himuon_version"]
@@ -69,6 +71,9 @@ def _load():
                                   P(ctypes.c_float), ctypes.c_int, ctypes.c_float, ctypes.c_void_p,
                                   ctypes.c_size_t, ctypes.c_void_p]
     L.himuon_tiled_ns.restype = ctypes.c_int
+    L.himuon_tiled_ns_noalloc.argtypes = [P(himuon_matrix_t), ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                          P(ctypes.c_float), ctypes.c_int, ctypes.c_float, ctypes.c_void_p]
+    L.himuon_tiled_ns_noalloc.restype = ctypes.c_int
     L.himuon_tiled_ns_schedule.argtypes = [P(himuon_matrix_t), ctypes.c_int32, P(ctypes.c_int32), ctypes.c_int32,
                                            P(ctypes.c_float), ctypes.c_int, ctypes.c_float, ctypes.c_void_p,
                                            ctypes.c_size_t, ctypes.c_void_p]
@@ -217,6 +222,20 @@ def himuon_tiled_ns(mats: Sequence, T: int, K: int, abc=(3.4445, -4.7750, 2.0315
                                ctypes.c_void_p(ptr), nbytes, _stream_handle(stream))
     _check(code, "himuon_tiled_ns")
     return ws
+
+
+def himuon_tiled_ns_noalloc(mats: Sequence, T: int, K: int, abc=(3.4445, -4.7750, 2.0315), eps: float = 1e-7,
+                            stream=None):
+    """Tiled Newton-Schulz in place, with no device allocation: the step path
+    runs through the library's own 128 MiB scratch on the device.  Calls that
+    overlap in time on one device race on that scratch."""
+    if len(mats) == 0:
+        return
+    dtype = _dtype_code(mats[0])
+    d = _descs(mats)
+    code = lib.himuon_tiled_ns_noalloc(d, len(mats), T, K, coeff_array(abc, K), dtype, eps,
+                                       _stream_handle(stream))
+    _check(code, "himuon_tiled_ns_noalloc")
 
 
 def himuon_tiled_ns_schedule(mats: Sequence, Ts: Sequence[int], abc=(3.4445, -4.7750, 2.0315), eps: float = 1e-7,

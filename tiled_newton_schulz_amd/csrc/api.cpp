@@ -719,6 +719,25 @@ himuon_status_t himuon_tiled_ns(const himuon_matrix_t* m, int32_t n, int32_t T, 
     return run(specs, T, K, abc, dt, eps, 0.f, 0.f, false, workspace, workspace_bytes, stream);
 }
 
+himuon_status_t himuon_tiled_ns_noalloc(const himuon_matrix_t* m, int32_t n, int32_t T, int32_t K,
+                                        const float* abc, himuon_dtype_t dt, float eps, void* stream) {
+    static_assert(HIMUON_NOALLOC_SCRATCH_BYTES == kStaticScratchBytes, "scratch size");
+    himuon_status_t st = check_common(n, T, K, dt, eps);
+    if (st != HIMUON_OK) return st;
+    if ((st = check_abc(K, abc)) != HIMUON_OK) return st;
+    std::vector<MatSpec> specs;
+    if ((st = gather(nullptr, m, nullptr, n, T, dt, specs)) != HIMUON_OK) return st;
+    // Size check before the device is touched: every tile of the step path
+    // must fit the scratch on its own (run() repeats this plan).
+    Plan plan;
+    if ((st = build_plan(specs, T, K, dt, kStaticScratchBytes, true, plan)) != HIMUON_OK) return st;
+    if (specs.empty()) return HIMUON_OK;
+    void* scratch = nullptr;
+    const hipError_t e = static_scratch(&scratch);
+    if (e != hipSuccess) return hip_fail(e);
+    return run(specs, T, K, abc, dt, eps, 0.f, 0.f, false, scratch, kStaticScratchBytes, stream);
+}
+
 himuon_status_t himuon_tiled_ns_schedule(const himuon_matrix_t* m, int32_t n, const int32_t* T, int32_t K,
                                          const float* abc, himuon_dtype_t dt, float eps, void* workspace,
                                          size_t workspace_bytes, void* stream) {

@@ -8,6 +8,9 @@ namespace himuon {
 
 constexpr int kMaxSteps = 16;     // largest K (matches HIMUON_MAX_STEPS)
 constexpr int kGroup = 256;       // tile classes per launch (kernel-argument table, ~25 KB)
+// Bytes of the library's own device scratch (himuon_tiled_ns_noalloc; matches
+// HIMUON_NOALLOC_SCRATCH_BYTES).
+constexpr size_t kStaticScratchBytes = size_t(128) << 20;
 
 // One tile class of one matrix in a launch: a rectangular block of the
 // matrix's tile grid whose tiles all have the same size th x tw (the interior
@@ -128,5 +131,8 @@ hipError_t launch_step_gram(const StepArgs& a, hipStream_t s);
 hipError_t launch_step_poly(const StepArgs& a, hipStream_t s);
 hipError_t launch_step_apply(const StepArgs& a, hipStream_t s);
 hipError_t launch_step_product(const StepArgs& a, hipStream_t s);
+// Device address of the library's scratch array on the current device
+// (static_scratch.hip); looked up once per device.
+hipError_t static_scratch(void** out);
 
 }  // namespace himuon
