@@ -48,7 +48,8 @@
  *   tiles, fp32 data, and the full-matrix map (T >= max(rows, cols)) run step
  *   by step through the caller's workspace, in chunks of tiles that each fit
  *   in `workspace_bytes`; that workspace is bf16 for bf16 tiles whose sides
- *   are both at least 64, fp32 otherwise.
+ *   are both at least 64, fp32 otherwise.  HIMUON_BF16_PRECISE runs every
+ *   tile on the step-by-step path with an fp32 workspace.
  */
 #ifndef HIMUON_H
 #define HIMUON_H
@@ -71,9 +72,40 @@ typedef struct himuon_matrix {
     int64_t ld;    /* row stride in elements, ld >= cols                     */
 } himuon_matrix_t;
 
+/*
+ * Storage and arithmetic.  The pages cast the normalised block to bf16 and
+ * leave later precision open ("Gram Newton-Schulz" page, section 3,
+ * Algorithm 1; section 6 notes on low-precision Gram iterations).
+ *
+ * Accuracy contract: the error of a tile is ||out - ref||_F / ||ref||_F with
+ * ref the exact (fp64) map of the stored input; the bound is on the worst tile.
+ *  - HIMUON_FP32: <= 1e-4 (measured at most a few 1e-6).
+ *  - HIMUON_BF16: <= 3e-2 (measured 1.1e-2 to 2.0e-2 on the worst of 10^4 to
+ *    10^6 random full-rank tiles per kernel size) for
+ *      * K <= 5 steps of the quintic (3.4445, -4.7750, 2.0315), or those
+ *        followed by converging steps such as the cubic (1.5, -0.5, 0), up
+ *        to K = 16;
+ *      * tiles without near-zero singular values (relative to the largest);
+ *      * entries of magnitude about 1e-15 to 1e15 (tested at 2^-50 and
+ *        2^50, with eps scaled to the data): the Frobenius reduction, and at
+ *        kernel tile 128 the product X X^T of the raw tile, run in fp32 and
+ *        underflow below about 1e-18 or overflow above about 1e17.
+ *    It does NOT hold for tiles of low numerical rank (rank 1 to 16 of a
+ *    128-tile: 0.17-0.29 measured), because the iterate is rounded to bf16
+ *    every step and each step multiplies its small singular values by about
+ *    a_t; nor for 16 quintic steps in a row (0.04-0.18 measured, by kernel
+ *    size; the quintic keeps singular values where its slope exceeds 1, so
+ *    every rounding grows from step to step).
+ *  - HIMUON_BF16_PRECISE: bf16 storage, fp32 arithmetic throughout (the
+ *    fp32 step-by-step path, fp32 MFMA); the result is rounded to bf16 once.
+ *    <= 3e-2 also on the cases above (measured 1.7e-3 to 2.0e-3, mostly the
+ *    final rounding), at a much lower throughput.  For calls whose tiles may
+ *    be of low rank or that run many quintic steps.
+ */
 typedef enum himuon_dtype {
-    HIMUON_BF16 = 0,   /* bfloat16 storage; bf16 MFMA with fp32 accumulation  */
-    HIMUON_FP32 = 1    /* float32 storage; fp32 arithmetic throughout         */
+    HIMUON_BF16 = 0,          /* bfloat16 storage; bf16 MFMA with fp32 accumulation */
+    HIMUON_FP32 = 1,          /* float32 storage; fp32 arithmetic throughout        */
+    HIMUON_BF16_PRECISE = 2   /* bfloat16 storage; fp32 arithmetic throughout       */
 } himuon_dtype_t;
 
 typedef enum himuon_status {

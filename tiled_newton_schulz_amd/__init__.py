@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(_HERE, "libhimuon.so")
 
 BF16 = 0
 FP32 = 1
+BF16_PRECISE = 2   # bf16 storage, fp32 arithmetic throughout
 MAX_STEPS = 16
 
 STATUS = {0: "HIMUON_OK", 1: "HIMUON_ERR_INVALID_ARGUMENT", 2: "HIMUON_ERR_UNSUPPORTED",
@@ -108,10 +109,10 @@ lib = _load()
 
 
 # ---- marshalling helpers -------------------------------------------------
-def _dtype_code(t) -> int:
+def _dtype_code(t, precise: bool = False) -> int:
     import torch
     if t.dtype == torch.bfloat16:
-        return BF16
+        return BF16_PRECISE if precise else BF16
     if t.dtype == torch.float32:
         return FP32
     raise TypeError(f"unsupported dtype {t.dtype}; use bfloat16 or float32")
@@ -208,14 +209,15 @@ def _workspace(mats, T, dtype, workspace, workspace_bytes, device):
 
 
 def himuon_tiled_ns(mats: Sequence, T: int, K: int, abc=(3.4445, -4.7750, 2.0315), eps: float = 1e-7,
-                    workspace=None, workspace_bytes: int | None = None, stream=None):
+                    workspace=None, workspace_bytes: int | None = None, stream=None, precise: bool = False):
     """Tiled Newton-Schulz in place on a list of 2-D bf16 or fp32 CUDA tensors.
 
     workspace: optional uint8 device tensor; if omitted the binding allocates
-    one through torch (capped at workspace_bytes when given)."""
+    one through torch (capped at workspace_bytes when given).  precise: bf16
+    data with fp32 arithmetic throughout (HIMUON_BF16_PRECISE)."""
     if len(mats) == 0:
         return
-    dtype = _dtype_code(mats[0])
+    dtype = _dtype_code(mats[0], precise)
     d = _descs(mats)
     ws, ptr, nbytes = _workspace(mats, T, dtype, workspace, workspace_bytes, mats[0].device)
     code = lib.himuon_tiled_ns(d, len(mats), T, K, coeff_array(abc, K), dtype, eps,
@@ -239,12 +241,12 @@ def himuon_tiled_ns_noalloc(mats: Sequence, T: int, K: int, abc=(3.4445, -4.7750
 
 
 def himuon_tiled_ns_schedule(mats: Sequence, Ts: Sequence[int], abc=(3.4445, -4.7750, 2.0315), eps: float = 1e-7,
-                             workspace=None, workspace_bytes: int | None = None, stream=None):
+                             workspace=None, workspace_bytes: int | None = None, stream=None, precise: bool = False):
     """len(Ts) Newton-Schulz steps in place, step k on the Ts[k] x Ts[k] tiles
     (non-increasing, nested sizes; one normalisation, on the first size)."""
     if len(mats) == 0:
         return
-    dtype = _dtype_code(mats[0])
+    dtype = _dtype_code(mats[0], precise)
     d = _descs(mats)
     K = len(Ts)
     ts = (ctypes.c_int32 * max(1, K))(*[int(t) for t in Ts])
@@ -266,14 +268,14 @@ def himuon_tiled_ns_schedule(mats: Sequence, Ts: Sequence[int], abc=(3.4445, -4.
 
 def himuon_muon_step(W: Sequence, M: Sequence, G: Sequence, T: int, K: int, abc=(3.4445, -4.7750, 2.0315),
                      mu: float = 0.95, eta: float = 0.02, eps: float = 1e-7, workspace=None,
-                     workspace_bytes: int | None = None, stream=None):
+                     workspace_bytes: int | None = None, stream=None, precise: bool = False):
     """Fused Muon step M <- mu M + G, W <- W - eta tiledNS(M), in place."""
     n = len(M)
     if not (len(W) == len(G) == n):
         raise ValueError("W, M, G must have equal length")
     if n == 0:
         return
-    dtype = _dtype_code(M[0])
+    dtype = _dtype_code(M[0], precise)
     dW, dM, dG = _descs(W), _descs(M), _descs(G)
     ws, ptr, nbytes = _workspace(M, T, dtype, workspace, workspace_bytes, M[0].device)
     code = lib.himuon_muon_step(dW, dM, dG, n, T, K, coeff_array(abc, K), mu, eta, dtype, eps,
@@ -294,12 +296,12 @@ def himuon_gram_ns_workspace(mats: Sequence, dtype: int | None = None) -> tuple[
 
 
 def himuon_gram_ns(mats: Sequence, K: int, abc=(3.4445, -4.7750, 2.0315), restart: int = 2, eps: float = 1e-7,
-                   workspace=None, workspace_bytes: int | None = None, stream=None):
+                   workspace=None, workspace_bytes: int | None = None, stream=None, precise: bool = False):
     """Full-matrix Newton-Schulz of each matrix, in place, through its Gram
     matrix with a restart before step restart + 1 (0: none)."""
     if len(mats) == 0:
         return
-    dtype = _dtype_code(mats[0])
+    dtype = _dtype_code(mats[0], precise)
     d = _descs(mats)
     if workspace is None:
         full = himuon_gram_ns_workspace(mats, dtype)[0]

@@ -24,7 +24,9 @@ thread_local int32_t g_last_hip = 0;
 constexpr int kWgNormMax = 32;
 constexpr size_t kAlign = 256;
 
-size_t elem_size(himuon_dtype_t dt) { return dt == HIMUON_BF16 ? 2 : 4; }
+size_t elem_size(himuon_dtype_t dt) { return dt == HIMUON_FP32 ? 4 : 2; }
+// Storage is bf16 for HIMUON_BF16 and HIMUON_BF16_PRECISE.
+bool bf16_storage(himuon_dtype_t dt) { return dt != HIMUON_FP32; }
 size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 
 struct MatSpec {
@@ -97,7 +99,7 @@ Extent extent_of(const himuon_matrix_t& d, size_t es, int id) {
 himuon_status_t check_common(int32_t n, int32_t T, int32_t K, himuon_dtype_t dt, float eps) {
     if (n < 0 || T < 1) return HIMUON_ERR_INVALID_ARGUMENT;
     if (K < 0 || K > HIMUON_MAX_STEPS) return HIMUON_ERR_INVALID_ARGUMENT;
-    if (dt != HIMUON_BF16 && dt != HIMUON_FP32) return HIMUON_ERR_UNSUPPORTED;
+    if (dt != HIMUON_BF16 && dt != HIMUON_FP32 && dt != HIMUON_BF16_PRECISE) return HIMUON_ERR_UNSUPPORTED;
     if (!(eps >= 0.f) || !std::isfinite(eps)) return HIMUON_ERR_INVALID_ARGUMENT;
     return HIMUON_OK;
 }
@@ -120,7 +122,7 @@ himuon_status_t check_abc(int32_t K, const float* abc) {
 //   bf16, a side < 32, both <= 64     -> on-chip kernel, hi/lo split precision
 //   bf16, both sides >= 64, one > 256 -> step path, bf16 workspace
 //   bf16, other thin tiles            -> step path, fp32 workspace
-//   fp32                              -> step path, fp32 workspace
+//   fp32, and bf16 with fp32 math     -> step path, fp32 workspace
 // A bf16 iterate of a tile whose short side r is small and whose long side s
 // is long loses accuracy.  Emulated worst errors, with a 3e-2 bound:
 //   on chip:   2.6e-2 at r = 32, s = 256; 2.1e-2 at r = 32, s = 128 and at
@@ -136,7 +138,7 @@ enum class Route { OnChip, OnChipPrecise, StepBf16, StepFp32 };
 
 Route route_of(himuon_dtype_t dt, int32_t th, int32_t tw) {
     const int32_t mn = std::min(th, tw), mx = std::max(th, tw);
-    if (dt == HIMUON_FP32) return Route::StepFp32;
+    if (dt == HIMUON_FP32 || dt == HIMUON_BF16_PRECISE) return Route::StepFp32;
     if (mx <= 256 && (mn >= 48 || (mn >= 32 && mx <= 128))) return Route::OnChip;
     if (mx <= 64) return Route::OnChipPrecise;
     if (mn >= 64) return Route::StepBf16;
@@ -237,7 +239,7 @@ himuon_status_t build_plan(const std::vector<MatSpec>& specs, int32_t T, int32_t
 
     // step path workspace dtype of a class: 0 bf16, 1 fp32, -1 on chip
     auto step_wk = [&](const TileClass& c) {
-        if (gram) return (dt == HIMUON_FP32 || std::min(c.th, c.tw) < 96) ? 1 : 0;
+        if (gram) return (dt != HIMUON_BF16 || std::min(c.th, c.tw) < 96) ? 1 : 0;
         const Route r = route_of(dt, c.th, c.tw);
         return r == Route::StepBf16 ? 0 : r == Route::StepFp32 ? 1 : -1;
     };
@@ -464,7 +466,7 @@ void chunk_args(const std::vector<MatSpec>& specs, const Plan& plan, const Chunk
     a.nb_max = (c.rmax + 127) / 128;
     a.ns_max = (c.smax + 127) / 128;
     a.wg_norm = std::min(kWgNormMax, std::max(1, c.sbmax));
-    a.io_dtype = dt == HIMUON_BF16 ? 0 : 1;
+    a.io_dtype = bf16_storage(dt) ? 0 : 1;
     a.wk_dtype = G.wk;
     a.muon = muon ? 1 : 0;
     a.eps = eps;
@@ -833,7 +835,7 @@ himuon_status_t himuon_pair_stats_workspace(const himuon_matrix_t* a, int32_t n,
 
 himuon_status_t himuon_pair_stats(const himuon_matrix_t* a, const himuon_matrix_t* b, int32_t n, himuon_dtype_t dt,
                                   double* out, void* workspace, size_t workspace_bytes, void* stream) {
-    if (dt != HIMUON_BF16 && dt != HIMUON_FP32) return HIMUON_ERR_UNSUPPORTED;
+    if (dt != HIMUON_BF16 && dt != HIMUON_FP32 && dt != HIMUON_BF16_PRECISE) return HIMUON_ERR_UNSUPPORTED;
     if (n < 0) return HIMUON_ERR_INVALID_ARGUMENT;
     if (n == 0) return HIMUON_OK;
     if (a == nullptr || b == nullptr || out == nullptr) return HIMUON_ERR_INVALID_ARGUMENT;
@@ -857,7 +859,7 @@ himuon_status_t himuon_pair_stats(const himuon_matrix_t* a, const himuon_matrix_
     for (int32_t g0 = 0; g0 < n; g0 += kPairGroup) {
         PairArgs pa{};
         pa.n = std::min<int32_t>(kPairGroup, n - g0);
-        pa.dtype = dt == HIMUON_BF16 ? 0 : 1;
+        pa.dtype = bf16_storage(dt) ? 0 : 1;
         pa.partial = reinterpret_cast<double*>(workspace);
         pa.out = out + 3 * (int64_t)g0;
         int32_t blocks = 0;
