@@ -35,6 +35,10 @@ The submodule ``oracle.diagnostics`` holds the tiled-versus-full-map measures
 (distance, cosine, output spectrum), pinned by
 ``tests/test_oracle_diagnostics.py``.
 
+``ns_map_stack_torch`` runs the same steps with torch CPU float64 batched
+products, for checks over whole workloads; it is pinned against ``ns_map``
+and the SVD closed form.
+
 Parity status: every function below is pinned by ``tests/test_oracle.py``
 (SVD closed form, independent full-matrix form, exact rational brute force,
 tile independence, transpose symmetry, zero padding, closed forms for rank-1,
@@ -45,6 +49,7 @@ from .tiled_ns import (  # noqa: F401
     QUINTIC_COEFFS,
     ns_map,
     ns_map_stack,
+    ns_map_stack_torch,
     full_matrix_ns,
     tile_grid,
     tiled_ns,

@@ -91,6 +91,30 @@ def ns_map_stack(Ys, coeffs, eps: float = EPS_DEFAULT, K: int | None = None):
     return np.ascontiguousarray(X)
 
 
+def ns_map_stack_torch(Ys, coeffs, eps: float = EPS_DEFAULT, K: int | None = None):
+    """ns_map on every block of an (N, h, w) stack, with torch CPU float64
+    batched products in place of numpy's (same steps and order as ns_map;
+    torch runs the batch on all host threads).  Takes and returns a torch
+    float64 CPU tensor; used to check whole workloads of 10^5 - 10^6 tiles."""
+    import torch
+    steps = _coeff_list(coeffs, K)
+    X = torch.as_tensor(Ys, dtype=torch.float64, device="cpu").clone()
+    if X.dim() != 3:
+        raise ValueError("ns_map_stack_torch takes an (N, h, w) stack")
+    norms = torch.sqrt(torch.sum(X * X, dim=(1, 2)))
+    X = X / (norms + eps)[:, None, None]
+    transposed = X.shape[1] > X.shape[2]
+    if transposed:
+        X = X.transpose(1, 2)
+    for a, b, c in steps:
+        A = torch.bmm(X, X.transpose(1, 2))
+        B = b * A + c * torch.bmm(A, A)
+        X = a * X + torch.bmm(B, X)
+    if transposed:
+        X = X.transpose(1, 2)
+    return X.contiguous()
+
+
 def full_matrix_ns(M, coeffs, eps: float = EPS_DEFAULT, K: int | None = None):
     """Full-matrix Newton-Schulz, written independently of ns_map.
 

@@ -211,6 +211,22 @@ def test_stack_matches_single():
         np.testing.assert_allclose(got[i], ns_map(St[i], Q5), rtol=0, atol=1e-14)
 
 
+@pytest.mark.parametrize("shape,coeffs", [((9, 24, 40), MIXED), ((6, 40, 24), Q5), ((5, 32, 32), Q5)])
+def test_stack_torch_matches_single_and_svd(shape, coeffs):
+    """The torch batched form against ns_map block by block, and against the
+    SVD closed form U p(S) V^T of each normalised block."""
+    S = rng(21).standard_normal(shape)
+    S[1] *= 1e-3                       # scale does not matter
+    S[2] = 0.0                         # zero block stays zero
+    got = oracle.ns_map_stack_torch(S, coeffs).numpy()
+    for i in range(shape[0]):
+        np.testing.assert_allclose(got[i], ns_map(S[i], coeffs), rtol=0, atol=1e-13)
+        Y0 = S[i] / (np.linalg.norm(S[i]) + EPS_DEFAULT)
+        U, sv, Vt = np.linalg.svd(Y0, full_matrices=False)
+        np.testing.assert_allclose(got[i], (U * scalar_poly(sv, coeffs)) @ Vt, rtol=0, atol=1e-11)
+    assert not np.any(got[2])
+
+
 def test_tile_accessor_and_grid():
     X = rng(14).standard_normal((70, 45))
     T = 32
