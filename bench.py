@@ -5,10 +5,13 @@
 
 A step is one himuon_tiled_ns call over the whole workload (all matrices of
 the batch, every tile, all K Newton-Schulz steps), with the inputs already
-resident in HBM.  The default workload is one transformer layer at d = 2048
-in bf16 (Q, K, V, O 2048 x 2048, MLP 2048 x 5632, 2048 x 5632, 5632 x 2048),
-T = 128, K = 5, one batched launch.  Each timed step runs on the previous
-step's output; the work does not depend on the values.
+resident in HBM.  The default workload is the cross-layer batch of 24
+transformer layers at d = 2048 in bf16 (per layer Q, K, V, O 2048 x 2048 and
+MLP 2048 x 5632, 2048 x 5632, 5632 x 2048: 168 matrices, 1.23 G elements),
+T = 128, K = 5, batched into one on-chip launch plus a launch for the partial
+last round.  Each timed step runs on the previous step's output; the work does
+not depend on the values.  Warm-up runs at least --warmup steps and at least
+--warmup-seconds.
 
 Prints one JSON line: useful TFLOP/s counted as sum 6 H W T K (value),
 matrices/s, % of the bf16 MFMA peak, the roofline of the dominant kernel
@@ -30,6 +33,15 @@ METRIC = "tiled-NS TFLOP/s (6\u00b7H\u00b7W\u00b7T\u00b7K) and % bf16 MFMA peak;
 PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
 PEAK_FP32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
+# Context only (another method on another machine): the Gram Newton-Schulz
+# page reports its Gram iteration cutting orthogonalisation-step time by
+# 40-50 % against standard Newton-Schulz on Hopper/Blackwell-class GPUs
+# (contributions; speed-up table).
+CONTEXT = {"gram_ns_page_cut": "40-50 % less orthogonalisation-step time for Gram Newton-Schulz vs standard "
+                               "Newton-Schulz on Hopper/Blackwell-class GPUs, as the Gram Newton-Schulz page "
+                               "reports it (context only: different method and hardware; the in-run comparison "
+                               "here is bench.py --gram)",
+           "gram_ns_page_cut_pct": [40, 50]}
 
 
 def algorithmic_flops(shapes, T, K):
@@ -46,36 +58,101 @@ def algorithmic_flops(shapes, T, K):
     return tot
 
 
-def cpu_baseline(w, T, K, min_seconds=10.0, max_seconds=30.0):
-    """The fp64 oracle, as it stands, on whole matrices of the workload drawn on
-    the host, repeated until at least min_seconds have passed."""
-    import numpy as np
+CPU_SHARE = 16   # host cores of one GPU's share of the box
+_CPU_MATS = []    # the sampled matrices, drawn before the workers fork
+
+
+def _oracle_bands(job):
+    """Worker: the oracle on whole T-row bands of the sampled matrices (a band
+    is tiled exactly as inside its matrix), with BLAS held to one thread."""
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    bands, T, K = job
+    with threadpool_limits(limits=1):
+        t0 = time.time()
+        for i, r0 in bands:
+            oracle.tiled_ns(_CPU_MATS[i][r0:r0 + T], T, w_coeffs(), K=K)
+        return t0, time.time()
+
+
+def _device_fds():
+    """Open file descriptors of this process on GPU device nodes."""
+    out = []
+    try:
+        for fd in os.listdir("/proc/self/fd"):
+            try:
+                tgt = os.readlink(f"/proc/self/fd/{fd}")
+            except OSError:
+                continue
+            if tgt.startswith("/dev/kfd") or tgt.startswith("/dev/dri"):
+                out.append(tgt)
+    except OSError:
+        pass
+    return out
+
+
+def cpu_baseline(w, T, K, target_s=10.0):
+    """The fp64 oracle, as it stands, timed on the host cores: one worker
+    process per core (BLAS one thread each) with the tiles split between them
+    as whole T-row bands, plus a single-core figure.  Runs before this process
+    touches the GPU, so the forked workers hold no device state.  The sample is
+    the workload's first (up to) 7 matrices, taken as many times as fill about
+    target_s seconds at the single-core rate times the worker count; the
+    oracle's time does not depend on the values."""
+    import multiprocessing as mp
+
+    from threadpoolctl import threadpool_limits
 
     import oracle
     import workloads
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = os.cpu_count() or 1
-    mats = []
-    for i in range(len(w.shapes)):
-        mats.append(workloads.round_to(workloads.host_matrix(w, i), w.dtype).double().numpy())
-    done_shapes = []
-    t0 = time.perf_counter()
-    i = 0
-    while True:
-        oracle.tiled_ns(mats[i % len(mats)], T, w_coeffs(), K=K)
-        done_shapes.append(mats[i % len(mats)].shape)
-        i += 1
-        el = time.perf_counter() - t0
-        if el >= min_seconds or el >= max_seconds:
-            break
-    flops = sum(6.0 * h * ww * T * K for h, ww in done_shapes)
-    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{len(done_shapes)} whole matrices of the workload ({i} oracle calls, fp64 numpy, "
-                      f"{el:.1f} s), same T and K",
-            "matrices_per_s": len(done_shapes) / el}
+    affinity = len(os.sched_getaffinity(0))
+    cores = max(1, min(affinity, CPU_SHARE))
+    _CPU_MATS.clear()
+    nm = min(7, len(w.shapes))
+    for i in range(nm):
+        _CPU_MATS.append(workloads.round_to(workloads.host_matrix(w, i), w.dtype).double().numpy())
+    # single core: bands of the first matrix for about 2 s
+    x0 = _CPU_MATS[0]
+    done, t0 = [], time.perf_counter()
+    with threadpool_limits(limits=1):
+        for r0 in range(0, x0.shape[0], T):
+            oracle.tiled_ns(x0[r0:r0 + T], T, w_coeffs(), K=K)
+            done.append(r0)
+            if time.perf_counter() - t0 >= 2.0:
+                break
+    t1 = time.perf_counter() - t0
+    single = algorithmic_flops([tuple(x0[r0:r0 + T].shape) for r0 in done], T, K) / t1
+    # all cores
+    bands = [(i, r0) for i in range(nm) for r0 in range(0, _CPU_MATS[i].shape[0], T)]
+    per_pass = sum(algorithmic_flops([tuple(_CPU_MATS[i][r0:r0 + T].shape)], T, K) for i, r0 in bands)
+    reps = max(1, int(round(single * cores * target_s / per_pass)))
+    bands = bands * reps
+    res = {"unit": "TFLOP/s", "kind": "oracle", "single_core_tflops": round(single / 1e12, 6),
+           "single_core_sample": f"{len(done)} T-row bands of matrix 0 {tuple(x0.shape)}, {t1:.1f} s, "
+                                 "one BLAS thread",
+           "affinity_cores": affinity}
+    held = _device_fds()
+    if held:
+        # never fork a process that holds the GPU: report the single core only
+        res.update({"value": round(single / 1e12, 6), "cores": 1,
+                    "sample": res["single_core_sample"] + f" (workers not started: {len(held)} device fds open)"})
+        _CPU_MATS.clear()
+        return res
+    jobs = [(bands[k::cores], T, K) for k in range(cores)]
+    with mp.get_context("fork").Pool(cores) as pool:
+        spans = pool.map(_oracle_bands, jobs, chunksize=1)
+    wall = max(e for _, e in spans) - min(b for b, _ in spans)
+    flops = per_pass * reps
+    elems = sum(m.size for m in _CPU_MATS)
+    _CPU_MATS.clear()
+    res.update({"value": round(flops / wall / 1e12, 5), "cores": cores,
+                "sample": f"{reps} pass(es) over the workload's first {nm} matrices ({elems:,} elements, "
+                          f"{len(bands)} T-row bands) on {cores} worker processes, one BLAS thread each, fp64 "
+                          f"numpy, {wall:.1f} s; same T and K",
+                "matrices_per_s": round(nm * reps / wall, 3), "gflops_fp64": round(flops / wall / 1e9, 2),
+                "wall_s": round(wall, 2)})
+    return res
 
 
 KERNEL_SOURCES = {
@@ -330,7 +407,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="layer_d2048")
+    ap.add_argument("--warmup-seconds", type=float, default=0.5,
+                    help="keep warming up until at least this long has passed (and --warmup steps have run)")
+    ap.add_argument("--workload", default="layers24_d2048")
     ap.add_argument("--T", type=int, default=None)
     ap.add_argument("--K", type=int, default=5)
     ap.add_argument("--cap", type=int, default=None, help="workspace cap in bytes")
@@ -353,6 +432,13 @@ def main():
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the tiled map has no "
               "exchange between GPUs, so one GPU's share is what is measured", file=sys.stderr)
         sys.exit(2)
+
+    # the CPU oracle first, before anything touches the GPU
+    cpu = None
+    if not (args.no_cpu or args.schedule or args.pair_stats or args.gram or args.copy_mib):
+        import workloads
+        wl = workloads.WORKLOADS[args.workload]
+        cpu = cpu_baseline(wl, args.T or wl.T, args.K)
 
     import torch
 
@@ -411,8 +497,15 @@ def main():
         else:
             H.himuon_tiled_ns(mats, T, K, workloads.COEFFS, workspace=ws, workspace_bytes=ws_bytes, stream=stream)
 
-    for _ in range(args.warmup):
+    # warm-up: at least --warmup steps and at least --warmup-seconds, so that
+    # a short --warmup still times the steady state (clocks up, code loaded)
+    t0 = time.perf_counter()
+    n_warm = 0
+    while n_warm < args.warmup or time.perf_counter() - t0 < args.warmup_seconds:
         step()
+        n_warm += 1
+        if n_warm % 8 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
@@ -460,14 +553,18 @@ def main():
                    "tiles": plan["tiles"], "tail_tiles": plan["tail_tiles"], "chunks": plan["chunks"],
                    "workspace_bytes": ws_bytes, "parallelism": "single GPU"},
         "matrices_per_s": round(len(shapes) / (ms_per_step * 1e-3), 1),
-        "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        # from the algorithmic count, which equals 6 H W T K for full tiles and
+        # stays meaningful for ragged tiles and T above the matrix size
+        "pct_bf16_peak": round(100.0 * alg / (ms_per_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
         "algorithmic_tflops": round(alg / (ms_per_step * 1e-3) / 1e12, 3),
         "hbm_gbs_io": round(io_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         "wall_ms_per_step": round(wall * 1e3 / args.steps, 5),
         "roofline": roof,
+        "warmup_steps_run": n_warm,
+        "context": CONTEXT,
     }
-    if not args.no_cpu and not sched:
-        out["cpu_baseline"] = cpu_baseline(w, T, K)
+    if cpu is not None:
+        out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)
 
 
