@@ -82,9 +82,11 @@ typedef struct himuon_matrix {
  *  - HIMUON_FP32: <= 1e-4 (measured at most a few 1e-6).
  *  - HIMUON_BF16: <= 3e-2 (measured 1.1e-2 to 2.0e-2 on the worst of 10^4 to
  *    10^6 random full-rank tiles per kernel size) for
- *      * K <= 5 steps of the quintic (3.4445, -4.7750, 2.0315), or those
- *        followed by converging steps such as the cubic (1.5, -0.5, 0), up
- *        to K = 16;
+ *      * K <= 5 steps (the quintic (3.4445, -4.7750, 2.0315) every step, or
+ *        per-step mixes with cubic steps); tiles of up to 32 also for longer
+ *        runs of converging steps, such as five quintic then eleven cubic
+ *        (1.5, -0.5, 0) steps, which larger tiles exceed on a tail of tiles
+ *        (1-3 % of random tiles, worst 0.15-0.25);
  *      * tiles without near-zero singular values (relative to the largest);
  *      * entries of magnitude about 1e-15 to 1e15 (tested at 2^-50 and
  *        2^50, with eps scaled to the data): the Frobenius reduction, and at

@@ -130,3 +130,36 @@ def test_precise_muon_step_and_gram(cuda):
     e = oracle.tile_rel_error(to_np(g), ref)
     say(f"precise gram: {e:.3e}")
     assert e <= 5e-3
+
+
+STEPS16 = [COEFFS] * 5 + [(1.5, -0.5, 0.0)] * 11
+
+
+@pytest.mark.parametrize("T,N", [(32, 48), (64, 12), (128, 16)])
+def test_damped_tail_many_tiles(cuda, T, N):
+    """Five quintic steps then eleven cubic ones over thousands of random
+    tiles.  Kernel tile 32 keeps the iterate in fp32 for such runs and stays
+    within the bound; the bf16 iterate of kernel tiles 64 and 128 exceeds it on
+    a tail of tiles whose small singular values the cubic steps keep
+    amplifying (emulated: 1.7 % of 64-tiles, 2.5 % of 128-tiles, worst
+    0.15-0.25), which the precise mode removes."""
+    gen = torch.Generator(device="cuda").manual_seed(61 + T)
+    mats = [torch.randn(1024, 1024, device="cuda", generator=gen).to(torch.bfloat16) for _ in range(N)]
+    nt = 1024 // T
+    host = np.stack([to_np(m) for m in mats]).reshape(N, nt, T, nt, T).transpose(0, 1, 3, 2, 4).reshape(-1, T, T)
+    ref = oracle.ns_map_stack_torch(host, STEPS16, K=16).numpy()
+    worst = {}
+    for precise in ((False,) if T == 32 else (False, True)):
+        devs = [m.clone() for m in mats]
+        H.himuon_tiled_ns(devs, T, 16, STEPS16, precise=precise)
+        torch.cuda.synchronize()
+        got = np.stack([to_np(m) for m in devs]).reshape(N, nt, T, nt, T).transpose(0, 1, 3, 2, 4).reshape(-1, T, T)
+        e = np.linalg.norm((got - ref).reshape(len(ref), -1), axis=1) / np.linalg.norm(ref.reshape(len(ref), -1), axis=1)
+        worst[precise] = float(e.max())
+        say(f"T={T} damped K=16 {'precise' if precise else 'bf16'}: {len(e)} tiles, worst {e.max():.3e}, "
+            f"over 3e-2: {(e > 3e-2).sum()}")
+    if T == 32:
+        assert worst[False] <= 3e-2
+    else:
+        assert 3e-2 < worst[False] < 0.6
+        assert worst[True] <= 5e-3

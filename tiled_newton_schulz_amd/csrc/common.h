@@ -45,6 +45,27 @@ struct ResidentArgs {
     int32_t normalize;   // 0: the tiles are used as they are (later runs of a tile-size schedule)
 };
 
+// Constants of the 32-tile kernel, which carries the iterate scaled, Y = g X
+// (resident32.hip).
+//  square = 1 (every step the same (a, b, c), c > 0; g = c^(1/4)):
+//    fp32 steps Y' = ra Y + (beta A + A^2) Y, bf16 steps
+//    Y' = ((A + mu I)^2 + d I) Y, with A = Y Y^T; the result is Y_K
+//    times rlast = 1 / g.
+//  square = 0: step k computes Y' = ra_k Y + (k1 A + k2 A^2) Y; in its bf16
+//    steps the identity enters the A^2 accumulator as dinit on the diagonal
+//    (quad clear: that accumulator is dinit I alone, k2 = 1).
+struct Consts32 {
+    float g0;                 // scale of the normalised tile
+    int32_t n_master;         // steps 0 .. n_master - 1 keep Y in fp32 with B split hi/lo
+    int32_t square;
+    float beta, mu, d, ra, rlast;
+    float k1[kMaxSteps];      // linear coefficient; exactly -1 or +1 within a run of equal b
+    float k2[kMaxSteps];      // quadratic coefficient
+    float ra_k[kMaxSteps];    // coefficient of Y
+    float dinit[kMaxSteps];   // identity term over k2 (bf16 steps)
+    int32_t quad;             // bit k: c_k != 0
+};
+
 // Arguments of the step-by-step path kernels for one chunk of tiles.
 struct StepArgs {
     MatEntry mats[kGroup];
@@ -123,6 +144,8 @@ __host__ __device__ inline TileGeom class_tile(const MatEntry& e, int32_t T, int
 hipError_t launch_resident(const ResidentArgs& a, int kernel_tile, bool muon, bool precise, bool narrow,
                            hipStream_t s);
 hipError_t launch_resident_coop(const ResidentArgs& a, bool muon, hipStream_t s);
+hipError_t launch_resident32(const ResidentArgs& a, bool muon, hipStream_t s);   // kernel tile 32, bf16 arithmetic
+Consts32 consts32(const float* abc, int K);
 hipError_t launch_resident256(const ResidentArgs& a, bool muon, bool narrow, hipStream_t s);
 int resident_slots(int kernel_tile, bool muon, bool precise);   // tiles the device holds at once (0 on error)
 int device_cus();

@@ -44,22 +44,6 @@
 
 #include "device_util.h"
 
-// Grid-stride launch of the kernel-tile-128 map, with each tile's load
-// overlapped with the step before (0: one workgroup per tile).
-#ifndef HIMUON_PERSIST128
-#define HIMUON_PERSIST128 1
-#endif
-// X' product of kernel tile 128 in units of two row blocks, each unit's
-// products interleaved with the previous unit's epilogue (0: the plain loop).
-#ifndef HIMUON_XUNITS
-#define HIMUON_XUNITS 1
-#endif
-// Kernel tile 128 (one-wave and eight-wave kernels alike) folds the tile's
-// normalisation into its first step (0: a separate scaling pass).
-#ifndef HIMUON_FOLD
-#define HIMUON_FOLD 1
-#endif
-
 namespace himuon {
 
 template <int TK, bool MUON, bool PRECISE>
@@ -83,15 +67,14 @@ void resident_kernel(const ResidentArgs args) {
     // stores of a tile drain while the next one starts, so that a wave's tile
     // I/O overlaps MFMA work instead of every wave of a round loading (and
     // storing) at the same time.
-    constexpr bool PERSIST = TK == 128 && !MUON && !PRECISE && HIMUON_PERSIST128;
-    constexpr bool XUNITS = HIMUON_XUNITS;
+    constexpr bool PERSIST = TK == 128 && !MUON && !PRECISE;
     // Kernel tile 128 folds the normalisation into the first step (K > 0):
     // the raw tile goes to LDS, the sum of squares is taken from the row
     // fragments of the first A product, and that step rounds s^2 A (the A of
     // the scaled tile) and scales the coefficients of B' by s, so that it
     // applies s B'(s^2 A) to the raw tile.  The eight-wave kernel does the
     // same, operation for operation.
-    constexpr bool FOLD = TK == 128 && HIMUON_FOLD;
+    constexpr bool FOLD = TK == 128;
     using FIRSTC = std::bool_constant<FOLD>;
 
     __shared__ __attribute__((aligned(16))) unsigned short sX[TK * LD];
@@ -500,7 +483,7 @@ void resident_kernel(const ResidentArgs args) {
                     if constexpr (SPLIT_X) opL[buf][K][f] = tr_frag(sXl, K, J, f);
                 }
         };
-        if constexpr (NB == 4 && XUNITS) {
+        if constexpr (NB == 4) {
             static_assert(!MASTER32 && !SPLIT_B && !SPLIT_X, "unit pipeline: bf16 tile, one product per block");
             // Units of work: unit u covers column block J = u / 2 and row blocks
             // I = 2 (u % 2), 2 (u % 2) + 1 (two interleaved chains).  Unit u's
@@ -621,7 +604,7 @@ void resident_kernel(const ResidentArgs args) {
         for (int it = 0; it < IO::NCH; ++it) chunk[it] = u16x8{};
     };
     if constexpr (PERSIST) {
-        static_assert(FOLD || !HIMUON_FOLD, "the grid-stride kernel is kernel tile 128");
+        static_assert(FOLD, "the grid-stride kernel is kernel tile 128");
         if (args.K >= 2) {
             ns_step(0, no_hook, FIRSTC{});
             for (int step = 1; step < args.K - 1; ++step) ns_step(step, no_hook, std::false_type{});
@@ -749,7 +732,7 @@ __global__ __launch_bounds__(512) void resident_coop_kernel(const ResidentArgs a
     // row-fragment order (lane l sums rows l % 32 + 32 I, columns
     // 16 kc + 8 (l / 32) .. + 7) once the first step's A products are issued.
     // With K = 0 it is taken here (lane l sums chunks l, l + 64, ...).
-    const bool fold = HIMUON_FOLD && args.K > 0;
+    const bool fold = args.K > 0;
     float scale = 1.0f;
     if (!fold) {
         if (w == 0) {
@@ -951,7 +934,7 @@ static hipError_t launch_tk(const ResidentArgs& a, hipStream_t s) {
     const int n = a.tile_end - a.tile_begin;
     if (n <= 0) return hipSuccess;
     int grid = n;
-    if constexpr (TK == 128 && !MUON && !PRECISE && HIMUON_PERSIST128) {
+    if constexpr (TK == 128 && !MUON && !PRECISE) {
         const int slots = persist_slots();
         if (slots > 0 && slots < n) grid = slots;
     }
@@ -969,7 +952,6 @@ int device_cus() {
 int resident_slots(int kernel_tile, bool muon, bool precise) {
     if (precise) return 0;
     switch (kernel_tile) {
-        case 32: return muon ? slots_tk<32, true, false>() : slots_tk<32, false, false>();
         case 64: return muon ? slots_tk<64, true, false>() : slots_tk<64, false, false>();
         case 128: return muon ? slots_tk<128, true, false>() : slots_tk<128, false, false>();
         default: return 0;
@@ -996,7 +978,7 @@ hipError_t launch_resident(const ResidentArgs& a, int kernel_tile, bool muon, bo
         }
     }
     switch (kernel_tile) {
-        case 32: return muon ? launch_tk<32, true, false>(a, s) : launch_tk<32, false, false>(a, s);
+        case 32: return launch_resident32(a, muon, s);
         case 64: return muon ? launch_tk<64, true, false>(a, s) : launch_tk<64, false, false>(a, s);
         case 128: return muon ? launch_tk<128, true, false>(a, s) : launch_tk<128, false, false>(a, s);
         case 256: return launch_resident256(a, muon, narrow, s);

@@ -280,38 +280,23 @@ __device__ __forceinline__ void store_out(const StepArgs& a, const MatEntry& me,
     }
 }
 
-#ifndef HIMUON_STEP_ASYNC
-#define HIMUON_STEP_ASYNC 1
-#endif
-#ifndef HIMUON_ASYNC_BK
-#define HIMUON_ASYNC_BK 32
-#endif
+// k chunk of the DMA GEMMs (elements)
+constexpr int kAsyncBK = 32;
 // Chunks whose largest tile has at least this many 128-row blocks run the
 // 256 x 256 block shape (measured on MI355X: the symmetric products gain from
 // r = 1024 on, 13 % at r = 2048 and 38 % for X X^T of an 8192 x 28672 matrix;
 // the apply product is level at r = s = 2048, 8 % faster at 2048 x 5632 and
 // 16 % at 8192 x 28672, and 6 % slower at r = s = 1024)
-#ifndef HIMUON_STEP_BIG_NB_SYM
-#define HIMUON_STEP_BIG_NB_SYM 8
-#endif
-#ifndef HIMUON_STEP_BIG_NB_APPLY
-#define HIMUON_STEP_BIG_NB_APPLY 16
-#endif
-// k chunk of the step GEMMs (tuning knobs; multiples of 32)
-#ifndef HIMUON_STEP_BK_BF16
-#define HIMUON_STEP_BK_BF16 64
-#endif
-#ifndef HIMUON_STEP_BK_FP32
-#define HIMUON_STEP_BK_FP32 32
-#endif
+constexpr int kBigNbSym = 8;
+constexpr int kBigNbApply = 16;
 template <int DT> struct GemmCfg;
 template <> struct GemmCfg<0> {
-    static constexpr int BK = HIMUON_STEP_BK_BF16, EPC = 8;         // k chunk, elements per 16-byte chunk
+    static constexpr int BK = 64, EPC = 8;         // k chunk, elements per 16-byte chunk
     static constexpr int LDP = BK + 8;             // row-panel stride (elements)
     static constexpr int LDN = 128 + 16;           // X-panel stride for apply
 };
 template <> struct GemmCfg<1> {
-    static constexpr int BK = HIMUON_STEP_BK_FP32, EPC = 4;
+    static constexpr int BK = 32, EPC = 4;
     static constexpr int LDP = BK + 1;
     static constexpr int LDN = 128 + 4;
 };
@@ -743,7 +728,7 @@ __global__ __launch_bounds__(AsyncShape<BIG>::NT) void step_gemm_async(const Ste
     constexpr int WNW = S::WNW;                      // waves along n (two along m)
     constexpr int FM = S::FM, FN = 2;                // 32 x 32 MFMA blocks of a wave along m and n
     constexpr int WR = 32 * FM;                      // rows of a wave's tile (its columns: 64)
-    constexpr int BK = HIMUON_ASYNC_BK;
+    constexpr int BK = kAsyncBK;
     constexpr int STAGE = BE * BK;                   // elements per operand and stage
     constexpr int CPR = BK / 8;                      // 16-byte chunks per panel row
     constexpr int NPI = BE * CPR / NT;               // DMA instructions per thread and operand
@@ -1162,8 +1147,8 @@ static hipError_t launch_gemm(const StepArgs& a, hipStream_t s) {
     // the direct-to-LDS kernel addresses an operand with 32-bit byte offsets
     const int64_t rmax = 128LL * a.nb_max, smax = 128LL * a.ns_max;
     const bool small = rmax * std::max(rmax, smax) * 2 < (1LL << 31);
-    const int big_nb = MODE == 2 ? HIMUON_STEP_BIG_NB_APPLY : HIMUON_STEP_BIG_NB_SYM;
-    if (a.wk_dtype == 0 && small && HIMUON_STEP_ASYNC && a.nb_max >= big_nb) {
+    const int big_nb = MODE == 2 ? kBigNbApply : kBigNbSym;
+    if (a.wk_dtype == 0 && small && a.nb_max >= big_nb) {
         // 256 x 256 blocks: the grid counts blocks of that size
         StepArgs b = a;
         const int64_t nt = a.tile_end - a.tile_begin;
@@ -1171,7 +1156,7 @@ static hipError_t launch_gemm(const StepArgs& a, hipStream_t s) {
         const int64_t bpt = MODE == 2 ? nbm * nsm : nbm * (nbm + 1) / 2;
         b.grid_blocks = (int32_t)((nt * bpt + 7) / 8 * 8);
         hipLaunchKernelGGL((step_gemm_async<MODE, true>), dim3(b.grid_blocks), dim3(512), 0, s, b);
-    } else if (a.wk_dtype == 0 && small && HIMUON_STEP_ASYNC)
+    } else if (a.wk_dtype == 0 && small)
         hipLaunchKernelGGL((step_gemm_async<MODE, false>), dim3(a.grid_blocks), dim3(256), 0, s, a);
     else if (a.wk_dtype == 0)
         hipLaunchKernelGGL((step_gemm_kernel<0, MODE>), dim3(a.grid_blocks), dim3(256), 0, s, a);
