@@ -1,7 +1,8 @@
-"""Whole-workload parity: every tile of the one-layer and 24-layer workloads
-against the oracle, the error tail of the on-chip 256 kernel (square and
-narrow tiles) and of the 512 step path, and functional-block splitting of a
-fused Q|K|V tensor (CMuon) against the oracle.
+"""Whole-workload parity: every tile of the one-layer workload, the 24-layer
+batch (T = 32, 64, 128), the MoE batch (T = 256, ragged edges) and the dense
+layer (T = 512 under the 4 GiB cap) against the oracle; the error tail of the
+on-chip 256 kernel (square and narrow tiles) and of the 512 step path; and
+functional-block splitting of a fused Q|K|V tensor (CMuon) against the oracle.
 
 The oracle side of the large checks is ns_map_stack_torch (the per-tile map
 in torch CPU float64, all host threads), in chunks of whole matrices so that
@@ -81,6 +82,51 @@ def test_layers24_every_tile(cuda, T, n_tiles):
     n, worst = check_every_tile(inputs, mats, T)
     say(f"layers24 T={T}: {n} tiles, worst {worst:.3e}")
     assert n == n_tiles and worst <= TOL
+
+
+def test_moe64_every_tile(cuda):
+    """The MoE batch (64 experts, 4096 x 1408 and 1408 x 4096, T = 256): all
+    12,288 tiles, 10,240 square and 2,048 ragged 128 x 256 / 256 x 128 edge
+    tiles, against the oracle."""
+    w = WORKLOADS["moe64"]
+    mats = workloads.device_tensors(w)
+    inputs = [m.clone() for m in mats]
+    H.himuon_tiled_ns(mats, 256, 5, COEFFS)
+    torch.cuda.synchronize()
+    say("moe64 T=256: comparing")
+    worst, count = 0.0, 0
+    for i in range(0, len(mats), 16):
+        groups = {}
+        for x, g in zip(inputs[i:i + 16], mats[i:i + 16]):
+            h, w_ = x.shape
+            for r0 in range(0, h, 256):
+                for c0 in range(0, w_, 256):
+                    key = (min(256, h - r0), min(256, w_ - c0))
+                    groups.setdefault(key, ([], []))
+                    groups[key][0].append(x[r0:r0 + 256, c0:c0 + 256])
+                    groups[key][1].append(g[r0:r0 + 256, c0:c0 + 256])
+        for key, (xs, gs) in groups.items():
+            xt = torch.stack(xs).to("cpu", torch.float64)
+            gt = torch.stack(gs).to("cpu", torch.float64)
+            e = stack_errors(gt, oracle.ns_map_stack_torch(xt, COEFFS, K=5))
+            worst = max(worst, float(e.max()))
+            count += e.numel()
+    say(f"moe64 T=256: {count} tiles, worst {worst:.3e}")
+    assert count == 12288 and worst <= TOL
+
+
+def test_dense8192_t512_every_tile(cuda):
+    """The dense layer (8192 x 28672 and 28672 x 8192) at T = 512 under the
+    4 GiB workspace cap: all 1,792 tiles against the oracle."""
+    w = WORKLOADS["dense8192"]
+    mats = workloads.device_tensors(w)
+    inputs = [m.clone() for m in mats]
+    H.himuon_tiled_ns(mats, 512, 5, COEFFS, workspace_bytes=4 << 30)
+    torch.cuda.synchronize()
+    say("dense8192 T=512: comparing")
+    n, worst = check_every_tile(inputs, mats, 512, chunk_elems=32 << 20)
+    say(f"dense8192 T=512: {n} tiles, worst {worst:.3e}")
+    assert n == 1792 and worst <= TOL
 
 
 @pytest.mark.parametrize("kind", ["square", "wide", "tall"])
