@@ -210,6 +210,29 @@ def test_steps_without_quintic_term(cuda, dt, T):
     assert err <= TOL[dt]
 
 
+# One or two steps with other signs than the quintic's: c < 0, b = 0, b > 0,
+# a = 0.  So few steps do not converge, so a wrong sign or scale of any term
+# shows as an error of order one, not as a small change of a converged result.
+SIGN_STEPS = [
+    [(1.5, -0.7, -0.1)],
+    [(1.5, -0.7, -0.1), (2.0, -1.2, 0.3)],
+    [(1.2, 0.0, 0.4)],
+    [(1.0, 0.5, 0.0)],
+    [(0.0, 1.0, 0.0)],
+    [(0.5, 0.3, -0.2), (1.5, -0.5, 0.0)],
+]
+
+
+@pytest.mark.parametrize("T", [8, 32, 64, 128, 256, 512])
+def test_coefficient_signs(cuda, T):
+    rng = np.random.default_rng([62, T])
+    x = workloads.round_to(rng.standard_normal((2 * T + 17, T + 9)), "bf16")
+    for steps in SIGN_STEPS:
+        err, _ = full_check(x, T, "bf16", K=len(steps), abc=steps)
+        say(f"T={T} steps {steps}: {err:.3e}")
+        assert err <= 1e-2, (steps, err)
+
+
 def test_steps_without_quintic_term_one_wave_kernel(cuda):
     """Enough 128-tiles that most run in the one-wave kernel (a small call runs
     in the eight-wave kernel only)."""

@@ -56,14 +56,17 @@ struct ResidentArgs {
 //    (quad clear: that accumulator is dinit I alone, k2 = 1).
 struct Consts32 {
     float g0;                 // scale of the normalised tile
-    int32_t n_master;         // steps 0 .. n_master - 1 keep Y in fp32 with B split hi/lo
+    int32_t n_master;         // steps 0 .. n_master - 1 keep Y in fp32
     int32_t square;
     float beta, mu, d, ra, rlast;
     float k1[kMaxSteps];      // linear coefficient; exactly -1 or +1 within a run of equal b
     float k2[kMaxSteps];      // quadratic coefficient
     float ra_k[kMaxSteps];    // coefficient of Y
     float dinit[kMaxSteps];   // identity term over k2 (bf16 steps)
+    float kap[kMaxSteps];     // fp32 steps: scale of the Gram matrix before its rounding
+    float cb[kMaxSteps];      // fp32 steps: coefficient of Y in the inner factor
     int32_t quad;             // bit k: c_k != 0
+    int32_t neg;              // bit k: c_k < 0
 };
 
 // Arguments of the step-by-step path kernels for one chunk of tiles.

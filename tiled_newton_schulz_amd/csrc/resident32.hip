@@ -22,20 +22,24 @@
 //    factor 1 / g is applied with the last rounding.
 //  * General form (any coefficients): g = sqrt(|b|) (1 when b = 0); the
 //    linear coefficient is then exactly -1 or +1 within a run of equal b
-//    (a sign modifier on the fma).
+//    (a sign modifier on the fma).  Its fp32 steps scale the Gram matrix
+//    by kap before rounding it, kap^2 = r |c| / g^4, so that the quadratic
+//    coefficient is +-1 there too.
 //
-// Precision.  The first n_master steps keep Y in fp32 registers, Y' = r a Y
-// accumulated in fp32, B = r (beta A_Y + A_Y^2) (square form: no shift, which
-// would round the small early A_Y around a large diagonal) as a bf16 hi/lo
-// pair (B Y = B_hi Y + B_lo Y).  The later steps keep Y in bf16 with the
-// identity folded into the product.  Rounding noise that a bf16 step puts
-// into directions of small singular values is multiplied by roughly a_t by
-// every later step, so the host makes the bf16 steps only a final run whose
-// product of |a_t| stays at most 41 (three quintic steps).  CPU emulation of
-// these roundings over 200k random 32-tiles, five quintic steps: worst 1.52e-2
-// (square form, n_master 2), 1.62e-2 (general form), against 1.79e-2 with
-// every step in fp32 and no split of the shifted square; five quintic plus
-// eleven cubic steps keep every step in fp32 by that rule: 7.9e-3.
+// Precision.  The first n_master steps keep Y in fp32 registers and take
+// the step in nested form, Y' = r a Y + Ab Z with Z = bf16(cb Y + Ab Y) and
+// Ab = bf16(A_Y) (the square form's cb is beta): every bf16 rounding but
+// that of the Gram matrix lands in a factor that Ab multiplies from the
+// left, which scales it down by the small singular values in their
+// directions, and the step is an exact polynomial of the one rounded Ab.
+// It takes six MFMAs and no unpacking of bf16 values.  The later steps keep
+// Y in bf16 with the identity folded into the product.  Rounding noise that
+// a bf16 step puts into directions of small singular values is multiplied by
+// roughly a_t by every later step, so the host makes the bf16 steps only a
+// final run whose product of |a_t| stays at most 41 (three quintic steps).
+// CPU emulation of these roundings over 200k random 32-tiles, five quintic
+// steps: worst 1.41e-2 (n_master 2), against 1.52e-2 for the earlier fp32
+// step B = beta Ab + Ab^2 split into a bf16 hi/lo pair.
 //
 // Layouts (one 32 x 32 block per wave, v_mfma_f32_32x32x16_bf16):
 //   accumulator layout AL: lane l, register q holds M[rho(l,q)][l % 32],
@@ -46,13 +50,15 @@
 // symmetric) for both; Y'^T = Y^T B takes AL(Y), read from LDS with
 // ds_read_tr16_b64, and AL(B), and lands in RL(Y').
 //
-// Measured on MI355X (24 transformer layers, 1.2 M tiles, K = 5): 2.00 ms per
-// call against 2.46 ms for the earlier form (every step in fp32, one
-// workgroup per tile), with the HBM reads halved by the tile pairing below.
-// At 108-128 registers a SIMD holds four waves, and the waves' dependent
-// chains (MFMA, conversion, MFMA) rather than the vector issue now set the
-// time: loading the next tile during the current one was 5-8 % slower, LDS
-// row strides of 48 and 56 elements 1-2 % slower than 40.
+// Measured on MI355X (24 transformer layers, 1.2 M tiles, K = 5): 1.66 ms per
+// call.  Steps: 2.46 ms with every step in fp32 and one workgroup per tile;
+// 2.00 ms with the hi/lo fp32 step, the tile pairing below (HBM reads
+// halved) and four waves per SIMD; 1.72 ms with the nested fp32 step and the
+// two step loops; 1.66 ms with five waves per SIMD (at most 96 registers).
+// Six waves would spill.  Loading the next tile during the current one was
+// slower both into registers (5-8 %) and straight into LDS with
+// global_load_lds (7 %).  LDS row strides of 48 and 56 elements were 1-2 %
+// slower than 40.
 //
 // Workgroups go round-robin to the eight XCDs.  A 32-tile row is 64 bytes,
 // half a cache line, so horizontally adjacent tiles are given to workgroups
@@ -90,9 +96,10 @@ __device__ __forceinline__ float wave_sum_dpp(float v) {
 }
 
 template <bool MUON, bool SQUARE>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4))) void resident32_kernel(
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(MUON ? 4 : 5))) void resident32_kernel(
     const ResidentArgs args, const Consts32 cs) {
     __shared__ __attribute__((aligned(16))) unsigned short sX[32 * kLD32];
+    __shared__ __attribute__((aligned(16))) unsigned short sZ[32 * kLD32];
 
     const int lane = threadIdx.x;
     const int l32 = lane & 31, g = lane >> 5;
@@ -101,20 +108,20 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4))) void re
 
     // RL run m (= q / 4) of a lane: row l32, columns 8m + 4g .. + 3
     auto rl_off = [&](int m) { return l32 * kLD32 + 8 * m + 4 * g; };
-    auto put_rl = [&](const u32x4 (&fr)[2]) {
+    auto put_rl = [&](unsigned short* buf, const u32x4 (&fr)[2]) {
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             u32x2 v = {fr[m >> 1][2 * (m & 1)], fr[m >> 1][2 * (m & 1) + 1]};
-            *reinterpret_cast<u32x2*>(&sX[rl_off(m)]) = v;
+            *reinterpret_cast<u32x2*>(&buf[rl_off(m)]) = v;
         }
     };
     // AL operand f of the stored (row-major) matrix: two transposed 8-byte reads
-    auto tr_frag = [&](int f) {
+    auto tr_frag = [&](const unsigned short* buf, int f) {
         const int G = lane >> 4, i16 = lane & 15;
         const int col = 16 * (G & 1) + 4 * (i16 & 3);
         const int rowb = 16 * f + 4 * g + (i16 >> 2);
-        bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(&sX[rowb * kLD32 + col]));
-        bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(&sX[(rowb + 8) * kLD32 + col]));
+        bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(&buf[rowb * kLD32 + col]));
+        bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(&buf[(rowb + 8) * kLD32 + col]));
         return __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     };
     // constant diagonals of the square form
@@ -211,46 +218,53 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4))) void re
         }
         u32x4 XR[2];
         __syncthreads();
-        // fp32 step (k < n_master): B = r beta' A + r' A^2 as a hi/lo pair,
-        // Y' = ra Y + B_hi Y + B_lo Y.  form_b writes B from the A^2
-        // accumulator and the packed A.
-        auto m_step = [&](float ra, auto form_b) __attribute__((always_inline)) {
+        // fp32 step (k < n_master): with Ab = bf16(kappa A_Y) and s = +-1,
+        //     Y' = ca Y + Ab Z,   Z = bf16(cb Y + s Ab Y),
+        // the iterate accumulated in fp32.  Both products put their bf16
+        // rounding into a factor that Ab multiplies from the left, so in the
+        // directions of small singular values it arrives scaled by them; the
+        // map is an exact polynomial of the one rounded Gram matrix.  lin:
+        // c = 0, Y' = ca Y + Ab Y.
+        auto m_step = [&](float ca, float cb, float kap, bool lin, bool neg) __attribute__((always_inline)) {
             XR[0] = cvt8(Ym, 0);
             XR[1] = cvt8(Ym, 8);
-            put_rl(XR);
+            put_rl(sX, XR);
             f32x16 a = mfma32w(XR[0], XR[0], f32x16{});
             a = mfma32w(XR[1], XR[1], a);
+            if (kap != 1.0f) a = a * kap;
             const u32x4 Ab[2] = {cvt8(a, 0), cvt8(a, 8)};
-            f32x16 B;
-            form_b(Ab, B);
-            const u32x4 Bh[2] = {cvt8(B, 0), cvt8(B, 8)};
-            // B - B_hi (exact in fp32), rounded: the low part of the pair.
-            // (v_dot2_f32_bf16 against (-1, 0) would save the unpacking, but
-            // on gfx950 its result is not the exact fp32 value: measured, it
-            // put a 1.7 % error into a 32-term sum of squares.)
-            const u32x4 Bl[2] = {cvt8_lo(B, 0, Bh[0]), cvt8_lo(B, 8, Bh[1])};
             __syncthreads();
-            const u32x4 op0 = tr_frag(0), op1 = tr_frag(1);
-            f32x16 y = Ym * ra;
-            y = mfma32w(op0, Bh[0], y);
-            y = mfma32w(op0, Bl[0], y);
-            y = mfma32w(op1, Bh[1], y);
-            y = mfma32w(op1, Bl[1], y);
+            u32x4 op0 = tr_frag(sX, 0), op1 = tr_frag(sX, 1);
+            if (!lin) {
+                // Z^T = cb Y^T + Yb^T Ab lands in the row layout
+                f32x16 z = Ym * cb;
+                z = mfma32w(op0, Ab[0], z);
+                z = mfma32w(op1, Ab[1], z);
+                u32x4 ZR[2] = {cvt8(z, 0), cvt8(z, 8)};
+                if (neg) {
+                    // c < 0: Y' = ca Y - Ab (-cb Y + Ab Y), the sign on Z
+                    ZR[0] ^= 0x80008000u;
+                    ZR[1] ^= 0x80008000u;
+                }
+                put_rl(sZ, ZR);
+                __syncthreads();
+                op0 = tr_frag(sZ, 0);
+                op1 = tr_frag(sZ, 1);
+            }
+            f32x16 y = Ym * ca;
+            y = mfma32w(op0, Ab[0], y);
+            y = mfma32w(op1, Ab[1], y);
             Ym = y;
             __syncthreads();
         };
         // bf16 step (k >= n_master): B' from the packed A by form_b,
         // Y' = B' Y rounded to bf16 in XR
-        auto f_step = [&](bool first, auto make_b) __attribute__((always_inline)) {
-            if (first) {
-                XR[0] = cvt8(Ym, 0);
-                XR[1] = cvt8(Ym, 8);
-            }
-            put_rl(XR);
+        auto f_step = [&](auto make_b) __attribute__((always_inline)) {
+            put_rl(sX, XR);
             u32x4 Bb[2];
             make_b(Bb);
             __syncthreads();
-            const u32x4 op0 = tr_frag(0), op1 = tr_frag(1);
+            const u32x4 op0 = tr_frag(sX, 0), op1 = tr_frag(sX, 1);
             f32x16 y = mfma32w(op0, Bb[0], f32x16{});
             y = mfma32w(op1, Bb[1], y);
             XR[0] = cvt8(y, 0);
@@ -264,27 +278,23 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4))) void re
             return mfma32w(Ab[1], Ab[1], acc);
         };
 
+        // The fp32 steps, then the bf16 steps, as two loops: one loop with
+        // both kinds of step made the compiler copy the iterate between
+        // registers on every step.
+        const int km = K < cs.n_master ? K : cs.n_master;
         if constexpr (SQUARE) {
             // ---- square form: constant coefficients, c > 0 ----
             // (the factor 1 / g that brings the last iterate back to X is
             // applied with the final rounding, below)
-            const float beta = cs.beta;
-            for (int k = 0; k < K; ++k) {
-                if (k < cs.n_master) {
-                    m_step(cs.ra, [&](const u32x4 (&Ab)[2], f32x16& B) __attribute__((always_inline)) {
-                        const f32x16 acc = square_of(Ab, f32x16{});
-#pragma unroll
-                        for (int f = 0; f < 2; ++f)
-#pragma unroll
-                            for (int kk = 0; kk < 4; ++kk) {
-                                const int e = 8 * f + 2 * kk;
-                                B[e] = __builtin_fmaf(beta, lo_f(Ab[f][kk]), acc[e]);
-                                B[e + 1] = __builtin_fmaf(beta, hi_f(Ab[f][kk]), acc[e + 1]);
-                            }
-                    });
-                } else {
+            for (int k = 0; k < km; ++k) m_step(cs.ra, cs.beta, 1.0f, false, false);
+            if (km < K) {
+                XR[0] = cvt8(Ym, 0);
+                XR[1] = cvt8(Ym, 8);
+            }
+            for (int k = km; k < K; ++k) {
+                {
                     // (A_Y + mu I)^2 + d I: both diagonals start the accumulators
-                    f_step(k == cs.n_master, [&](u32x4 (&Bb)[2]) __attribute__((always_inline)) {
+                    f_step([&](u32x4 (&Bb)[2]) __attribute__((always_inline)) {
                         f32x16 z = mfma32w(XR[0], XR[0], CiMu);
                         z = mfma32w(XR[1], XR[1], z);
                         const u32x4 Zb[2] = {cvt8(z, 0), cvt8(z, 8)};
@@ -296,7 +306,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4))) void re
             }
         } else {
             // ---- general form ----
-            for (int k = 0; k < K; ++k) {
+            for (int k = 0; k < km; ++k)
+                m_step(cs.ra_k[k], cs.cb[k], cs.kap[k], !((cs.quad >> k) & 1), (cs.neg >> k) & 1);
+            if (km < K) {
+                XR[0] = cvt8(Ym, 0);
+                XR[1] = cvt8(Ym, 8);
+            }
+            for (int k = km; k < K; ++k) {
                 const float k1 = cs.k1[k], k2 = cs.k2[k];
                 const bool quad = (cs.quad >> k) & 1;
                 // B = kq acc + k1 A from the packed A
@@ -310,16 +326,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4))) void re
                             B[e + 1] = __builtin_fmaf(kq, acc[e + 1], k1 * hi_f(Ab[f][kk]));
                         }
                 };
-                if (k < cs.n_master) {
-                    m_step(cs.ra_k[k], [&](const u32x4 (&Ab)[2], f32x16& B) __attribute__((always_inline)) {
-                        if (quad) lin_b(square_of(Ab, f32x16{}), Ab, k2, B);
-                        else lin_b(f32x16{}, Ab, 0.f, B);
-                    });
-                } else {
+                {
                     // B' = r a I + k1 A + k2 A^2: the identity as the diagonal
                     // of the A^2 accumulator's start (dinit = r a / k2), or
                     // alone when c = 0 (k2 = 1, dinit = r a)
-                    f_step(k == cs.n_master, [&](u32x4 (&Bb)[2]) __attribute__((always_inline)) {
+                    f_step([&](u32x4 (&Bb)[2]) __attribute__((always_inline)) {
                         f32x16 a = mfma32w(XR[0], XR[0], f32x16{});
                         a = mfma32w(XR[1], XR[1], a);
                         const u32x4 Ab[2] = {cvt8(a, 0), cvt8(a, 8)};
@@ -342,7 +353,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4))) void re
         }
 
         // ---- write back in place (Muon: W <- W - eta X) ----
-        put_rl(XR);
+        put_rl(sX, XR);
         __syncthreads();
         u16x8 out[IO::NCH];
 #pragma unroll
@@ -421,6 +432,7 @@ Consts32 consts32(const float* abc, int K) {
     gk[K] = 1.0;
     c.g0 = (float)gk[0];
     c.quad = 0;
+    c.neg = 0;
     for (int k = 0; k < K; ++k) {
         const double ak = abc[3 * k], bk = abc[3 * k + 1], ck = abc[3 * k + 2];
         const double r = gk[k + 1] / gk[k];
@@ -433,9 +445,17 @@ Consts32 consts32(const float* abc, int K) {
             const double k2 = r * ck / (g2 * g2);
             c.k2[k] = (float)k2;
             c.dinit[k] = (float)(r * ak / k2);
+            // fp32 step: kap^2 = r |c| / g^4, kap cb = r b / g^2; for c < 0
+            // the kernel forms -Z = -cb Y + Ab Y and negates its rounding
+            const double kap = std::sqrt(r * std::fabs(ck)) / g2;
+            const double cb = r * bk / (g2 * kap);
+            c.kap[k] = (float)kap;
+            c.cb[k] = (float)(ck < 0.0 ? -cb : cb);
+            if (ck < 0.0) c.neg |= 1 << k;
         } else {
             c.k2[k] = 1.0f;
             c.dinit[k] = (float)(r * ak);
+            c.kap[k] = (float)(r * bk / g2);   // fp32 step: Y' = r a Y + Ab Y
         }
     }
     return c;
