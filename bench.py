@@ -156,11 +156,14 @@ def cpu_baseline(w, T, K, target_s=10.0):
 
 
 KERNEL_SOURCES = {
+    "resident32_kernel": ["resident32.hip", "device_util.h", "common.h"],
+    "resident_kernel<64>": ["resident.hip", "device_util.h", "common.h"],
     "resident_kernel<128>": ["resident.hip", "device_util.h", "common.h"],
     "resident256_kernel": ["resident256.hip", "device_util.h", "common.h"],
     "pair_stats": ["pair_stats.hip", "pair_stats.h"],
 }
-KERNEL_OF_TILE = {128: "resident_kernel<128>", 256: "resident256_kernel"}
+KERNEL_OF_TILE = {32: "resident32_kernel", 64: "resident_kernel<64>", 128: "resident_kernel<128>",
+                  256: "resident256_kernel"}
 
 
 def sources_sha(kernel):
@@ -207,7 +210,12 @@ def dominant_kernel_roofline(H, torch, mats, shapes, T, K, plan, stream, ms_per_
     on the launch stream.  A step that is one launch is timed as a whole; when a
     step is one on-chip launch plus a tail launch, the main launch alone is
     timed on the same matrices with the tail's tiles cut off (whole row bands),
-    which gives the same kernel the same tile count it runs in the step."""
+    which gives the same kernel the same tile count it runs in the step.  The
+    bound is the roofline with the longer floor for that work: MFMA (its
+    algorithmic flops at the dtype's peak) or HBM (one read and one write of
+    every element at 8 TB/s)."""
+    dsize = 2 if w.dtype == "bf16" else 4
+    nbytes = 2.0 * dsize * sum(h * ww for h, ww in shapes)
     kernel_tile = plan["kernel_tile"]
     main = KERNEL_OF_TILE.get(kernel_tile)
     one_launch = plan["chunks"] == 0 and plan["resident_launches"] == 1
@@ -229,11 +237,17 @@ def dominant_kernel_roofline(H, torch, mats, shapes, T, K, plan, stream, ms_per_
         torch.cuda.synchronize()
         kernel, tiles, ms = main, sub_plan["tiles"], e0.elapsed_time(e1) / n
         flops = algorithmic_flops([tuple(m.shape) for m in sub], T, K)
+        nbytes = 2.0 * dsize * sum(m.shape[0] * m.shape[1] for m in sub)
     else:
         kernel = f"whole step ({plan['launches']} launches)"
         tiles, ms, flops = plan["tiles"], ms_per_step, alg
-    achieved = flops / (ms * 1e-3) / 1e12
     traffic = recorded_traffic(kernel, w.name, T, tiles) if kernel in KERNEL_SOURCES else None
+    if nbytes / (PEAK_HBM_GBS * 1e9) > flops / (peak * 1e12):
+        achieved = nbytes / (ms * 1e-3) / 1e9
+        return {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic, "kernel": kernel, "tiles": tiles,
+                "launch_ms": round(ms, 5)}
+    achieved = flops / (ms * 1e-3) / 1e12
     return {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4), "traffic": traffic, "kernel": kernel, "tiles": tiles,
             "launch_ms": round(ms, 5)}
