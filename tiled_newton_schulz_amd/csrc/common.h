@@ -43,16 +43,24 @@ struct ResidentArgs {
     float eps;
     float mu, eta;       // Muon step only
     int32_t normalize;   // 0: the tiles are used as they are (later runs of a tile-size schedule)
+    // Kernel tiles 64 and 128 (not the split-precision variants): steps with
+    // bit k of sq_mask set run in square form, Z = A + sq_mu I rounded,
+    // B' = Z^2 + sq_d I, on an iterate the host has scaled (abc then holds the
+    // other steps' coefficients for that scaling; sym_schedule in resident.hip).
+    float sq_mu[kMaxSteps], sq_d[kMaxSteps];
+    int32_t sq_mask;
 };
 
 // Constants of the 32-tile kernel, which carries the iterate scaled, Y = g X
 // (resident32.hip).
 //  square = 1 (every step the same (a, b, c), c > 0; g = c^(1/4)):
-//    fp32 steps Y' = ra Y + (beta A + A^2) Y, bf16 steps
-//    Y' = ((A + mu I)^2 + d I) Y, with A = Y Y^T; the result is Y_K
+//    fp32 steps Y' = ra Y + Ab bf16(beta Y + Ab Y) with Ab = bf16(A), bf16
+//    steps Y' = ((A + mu I)^2 + d I) Y, with A = Y Y^T; the result is Y_K
 //    times rlast = 1 / g.
-//  square = 0: step k computes Y' = ra_k Y + (k1 A + k2 A^2) Y; in its bf16
-//    steps the identity enters the A^2 accumulator as dinit on the diagonal
+//  square = 0: fp32 step k computes Y' = ra_k Y + Ab Z with Ab =
+//    bf16(kap_k A) and Z = bf16(cb_k Y +- Ab Y) (the sign of c_k; c_k = 0:
+//    Y' = ra_k Y + Ab Y); bf16 step k computes Y' = ra_k Y + (k1 A + k2 A^2) Y,
+//    the identity entering the A^2 accumulator as dinit on the diagonal
 //    (quad clear: that accumulator is dinit I alone, k2 = 1).
 struct Consts32 {
     float g0;                 // scale of the normalised tile
@@ -146,6 +154,9 @@ __host__ __device__ inline TileGeom class_tile(const MatEntry& e, int32_t T, int
 // narrow: kernel tile 256 with the shorter tile side <= 128
 hipError_t launch_resident(const ResidentArgs& a, int kernel_tile, bool muon, bool precise, bool narrow,
                            hipStream_t s);
+// fp32 tiles of up to 64 x 64: one four-wave workgroup per tile, fp32 MFMA
+// (resident_f32.hip).
+hipError_t launch_resident_f32(const ResidentArgs& a, bool muon, hipStream_t s);
 hipError_t launch_resident_coop(const ResidentArgs& a, bool muon, hipStream_t s);
 hipError_t launch_resident32(const ResidentArgs& a, bool muon, hipStream_t s);   // kernel tile 32, bf16 arithmetic
 Consts32 consts32(const float* abc, int K);
