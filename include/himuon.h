@@ -44,12 +44,14 @@
  *   with both sides at most 64) stay resident on chip for all K steps and
  *   need no workspace: one kernel launch per group of up to 256 tile classes (a class
  *   is one matrix's interior, right-edge, bottom-edge or corner tiles), plus
- *   one for a partly filled last round of 128-tiles.  Larger tiles, thin
- *   tiles, fp32 data, and the full-matrix map (T >= max(rows, cols)) run step
- *   by step through the caller's workspace, in chunks of tiles that each fit
- *   in `workspace_bytes`; that workspace is bf16 for bf16 tiles whose sides
- *   are both at least 64, fp32 otherwise.  HIMUON_BF16_PRECISE runs every
- *   tile on the step-by-step path with an fp32 workspace.
+ *   one for a partly filled last round of 128-tiles.  fp32 tiles with both
+ *   sides at most 64 stay on chip too (fp32 MFMA, one launch per group).
+ *   Larger tiles, thin tiles, larger fp32 tiles, and the full-matrix map
+ *   (T >= max(rows, cols)) run step by step through the caller's workspace,
+ *   in chunks of tiles that each fit in `workspace_bytes`; that workspace is
+ *   bf16 for bf16 tiles whose sides are both at least 64, fp32 otherwise.
+ *   HIMUON_BF16_PRECISE runs every tile on the step-by-step path with an
+ *   fp32 workspace.
  */
 #ifndef HIMUON_H
 #define HIMUON_H

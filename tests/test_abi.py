@@ -129,6 +129,22 @@ def test_plan_layer_on_chip():
     assert info["tiles"] == 4 * 64 * 64 + 3 * 64 * 176 and info["kernel_tile"] == 32
 
 
+def test_plan_fp32_on_chip():
+    """fp32 tiles of up to 64 x 64 run in one on-chip launch with no workspace;
+    larger fp32 tiles take the step path."""
+    x = sd(256, 512, ptr=1 << 32)
+    info = H.himuon_plan([x], 64, 5, H.FP32)
+    assert info["tiles"] == 32 and info["resident_launches"] == 1 and info["chunks"] == 0
+    assert info["kernel_tile"] == 64 and info["workspace_full"] == 0
+    info = H.himuon_plan([sd(100, 70, ptr=1 << 32)], 48, 3, H.FP32)   # 48 and 22/4-wide edges
+    assert info["resident_launches"] == 1 and info["chunks"] == 0
+    info = H.himuon_plan([x], 128, 5, H.FP32, 1 << 30)
+    assert info["resident_launches"] == 0 and info["chunks"] >= 1 and info["workspace_full"] > 0
+    # bf16 storage with fp32 arithmetic keeps the step path
+    info = H.himuon_plan([sd(256, 512, ptr=1 << 32)], 64, 5, H.BF16_PRECISE, 1 << 30)
+    assert info["resident_launches"] == 0 and info["chunks"] >= 1
+
+
 def test_plan_cross_layer_groups():
     descs = layer_descs() * 1
     many = []
@@ -196,9 +212,9 @@ def test_plan_full_matrix_and_fp32():
     d = layer_descs()
     info = H.himuon_plan(d, 5632, 5, H.BF16, 1 << 40)
     assert info["tiles"] == 7 and info["resident_launches"] == 0 and info["chunks"] == 1
-    # fp32 data always takes the step path
-    info = H.himuon_plan([sd(256, 512)], 64, 5, H.FP32, 1 << 30)
-    assert info["tiles"] == 32 and info["chunks"] == 1 and info["launches"] == 2 + 15
+    # fp32 tiles larger than 64 take the step path
+    info = H.himuon_plan([sd(256, 512)], 128, 5, H.FP32, 1 << 30)
+    assert info["tiles"] == 8 and info["chunks"] == 1 and info["launches"] == 2 + 15
     # a bf16 matrix smaller than 128 at T = 256 stays on chip
     info = H.himuon_plan([sd(100, 90)], 256, 5, H.BF16)
     assert info["resident_launches"] == 1 and info["kernel_tile"] == 128

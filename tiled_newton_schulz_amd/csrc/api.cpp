@@ -134,10 +134,11 @@ struct TileClass {
     int64_t tiles() const { return (int64_t)n_ti * n_tj; }
 };
 
-enum class Route { OnChip, OnChipPrecise, StepBf16, StepFp32 };
+enum class Route { OnChip, OnChipPrecise, OnChipF32, StepBf16, StepFp32 };
 
 Route route_of(himuon_dtype_t dt, int32_t th, int32_t tw) {
     const int32_t mn = std::min(th, tw), mx = std::max(th, tw);
+    if (dt == HIMUON_FP32 && mx <= 64) return Route::OnChipF32;
     if (dt == HIMUON_FP32 || dt == HIMUON_BF16_PRECISE) return Route::StepFp32;
     if (mx <= 256 && (mn >= 48 || (mn >= 32 && mx <= 128))) return Route::OnChip;
     if (mx <= 64) return Route::OnChipPrecise;
@@ -173,6 +174,7 @@ struct Group {
     std::vector<int64_t> tile_base, xoff, aoff;
     int kernel_tile = 0;         // on-chip groups
     bool precise = false;        // on-chip groups
+    bool f32 = false;            // on-chip groups: fp32 data (kernel tile 64)
     bool narrow = false;         // on-chip kernel tile 256: shorter side <= 128
     int wk = 0;                  // step groups: workspace dtype (0 bf16, 1 fp32)
     int64_t tiles = 0;
@@ -245,24 +247,28 @@ himuon_status_t build_plan(const std::vector<MatSpec>& specs, int32_t T, int32_t
     };
     const int sq = gram ? 4 : 2;
 
-    // on-chip launches, keyed by (kernel tile, precision)
-    for (int precise = 0; precise < (gram ? 0 : 2); ++precise)
+    // on-chip launches, keyed by (kernel tile, kind): kind 0 bf16, 1 split
+    // precision, 2 fp32 data (every such tile in the kernel of tile 64)
+    for (int kind = 0; kind < (gram ? 0 : 3); ++kind)
         for (int kt : {32, 64, 128, 256})
           for (int narrow = 0; narrow < (kt == 256 ? 2 : 1); ++narrow) {
+            if (kind == 2 && kt != 64) continue;
             Group cur;
             cur.kernel_tile = kt;
-            cur.precise = precise != 0;
+            cur.precise = kind == 1;
+            cur.f32 = kind == 2;
             cur.narrow = narrow != 0;
             for (const TileClass& c : all) {
                 const Route r = route_of(dt, c.th, c.tw);
-                const bool on = precise ? r == Route::OnChipPrecise : r == Route::OnChip;
-                if (!on || kernel_tile_for(c.th, c.tw) != kt) continue;
+                const bool on = r == (kind == 0 ? Route::OnChip : kind == 1 ? Route::OnChipPrecise : Route::OnChipF32);
+                if (!on || (kind != 2 && kernel_tile_for(c.th, c.tw) != kt)) continue;
                 if (kt == 256 && (std::min(c.th, c.tw) <= 128) != (narrow != 0)) continue;
                 if ((int)cur.cls.size() == kGroup || cur.tiles + c.tiles() > INT32_MAX) {
                     plan.rgroups.push_back(cur);
                     cur = Group();
                     cur.kernel_tile = kt;
-                    cur.precise = precise != 0;
+                    cur.precise = kind == 1;
+                    cur.f32 = kind == 2;
                     cur.narrow = narrow != 0;
                 }
                 cur.cls.push_back(c);
@@ -433,7 +439,7 @@ SlotInfo slot_info(bool muon) {
 // device holds at once).  Returns the group's tile count when there is none.
 int32_t tail_split(const Group& G, bool muon) {
     const int32_t total = (int32_t)G.tiles;
-    if (G.kernel_tile != 128 || G.precise) return total;
+    if (G.kernel_tile != 128 || G.precise || G.f32) return total;
     const SlotInfo si = slot_info(muon);
     if (si.slots <= 0 || si.cus <= 0) return total;
     const int32_t rem = total % si.slots;
@@ -511,7 +517,8 @@ himuon_status_t run(const std::vector<MatSpec>& specs, int32_t T, int32_t K, con
         const int32_t split = tail_split(G, muon);
         a.tile_begin = 0;
         a.tile_end = split;
-        hipError_t e = launch_resident(a, G.kernel_tile, muon, G.precise, G.narrow, s);
+        hipError_t e = G.f32 ? launch_resident_f32(a, muon, s)
+                             : launch_resident(a, G.kernel_tile, muon, G.precise, G.narrow, s);
         if (e != hipSuccess) return hip_fail(e);
         if (split < a.total_tiles) {
             a.tile_begin = split;
