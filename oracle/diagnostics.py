@@ -21,8 +21,9 @@ follow from them, and from the matrices directly, in the functions below.
 
 Parity status: pinned by tests/test_oracle_diagnostics.py (brute-force sums,
 the identities of the two measures, the full map recovered at T >= max(H, W),
-the SVD closed form of the output spectrum, and a closed form of the
-tiled-to-full distance for block-diagonal inputs).
+the SVD closed form of the output spectrum, the spectral moments against
+trace identities of the Gram matrix, and a closed form of the tiled-to-full
+distance for block-diagonal inputs).
 """
 from __future__ import annotations
 
@@ -72,6 +73,22 @@ def cosine_from_stats(stats) -> float:
 def spectrum(X):
     """Singular values of X, largest first (LAPACK through numpy)."""
     return np.linalg.svd(np.asarray(X, dtype=np.float64), compute_uv=False)
+
+
+def spectral_moments(X):
+    """(r, sum s^2, sum s^4, sum s^6) over the r = min(H, W) singular values s
+    of X, from its spectrum.  With the moments, mean(s^2) = m2 / r and
+    ||X^T X - I||_F^2 = sum (s^2 - 1)^2 = m4 - 2 m2 + r (the Gram matrix of
+    the shorter side) measure how far an output is from orthogonal."""
+    X = np.asarray(X, dtype=np.float64)
+    s2 = spectrum(X) ** 2
+    return min(X.shape), float(np.sum(s2)), float(np.sum(s2 ** 2)), float(np.sum(s2 ** 3))
+
+
+def orthogonality_residual(moments) -> float:
+    """RMS of s^2 - 1 over the singular values: sqrt((m4 - 2 m2 + r) / r)."""
+    r, m2, m4, _ = moments
+    return math.sqrt(max(m4 - 2.0 * m2 + r, 0.0) / r) if r > 0 else 0.0
 
 
 def scalar_map(x, coeffs, K: int | None = None):

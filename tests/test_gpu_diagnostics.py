@@ -9,9 +9,14 @@
 * End to end against the oracle's fp64 maps: the bf16 path's per-tile error
   is at most 3e-2 of the tile norm (the parity bound), so by the triangle
   inequality ||tiled_gpu - full_gpu|| differs from ||tiled - full|| by at most
-  3e-2 (||tiled|| + ||full||); singular values move by at most the Frobenius
-  error (Weyl).
+  3e-2 (||tiled|| + ||full||); the vector of singular values moves by at
+  most the Frobenius error (Hoffman-Wielandt), which bounds the change of
+  the spectral moments.
+* The spectral moments the library computes with its own kernels against
+  closed forms for matrices with known singular values (fp32: 1e-5).
 """
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -118,9 +123,46 @@ def test_tiled_vs_full_against_oracle(cuda, shape, Ts):
         slack = 3e-2 * (np.linalg.norm(t_ref) + np.linalg.norm(full_ref)) / np.linalg.norm(full_ref)
         say(f"  T={T}: distance {row['distance']:.4f} (oracle {rr['distance']:.4f}), cosine {row['cosine']:.4f}")
         assert abs(row["distance"] - rr["distance"]) <= slack + 3e-2
-        weyl = 3e-2 * np.linalg.norm(t_ref)
-        assert np.max(np.abs(row["spectrum"][0].double().numpy() - rr["spectrum"])) <= weyl
+        check_moments(row["moments"][0], t_ref)
         if T >= max(shape):
             assert row["distance"] == 0.0 and row["cosine"] == pytest.approx(1.0, abs=1e-15)
-    weyl = 3e-2 * np.linalg.norm(full_ref)
-    assert np.max(np.abs(res["full_spectrum"][0].double().numpy() - ref[-1]["full_spectrum"])) <= weyl
+    check_moments(res["full_moments"][0], full_ref)
+
+
+def check_moments(got, ref_out):
+    """Moments of a library output against those of the oracle's output: the
+    singular values s (library) and t (oracle) satisfy ||s - t||_2 <= delta =
+    3e-2 ||ref||_F, so |sum s^k - sum t^k| <= k M^(k-1) sqrt(r) delta."""
+    want = OD.spectral_moments(ref_out)
+    r = want[0]
+    delta = 3e-2 * np.linalg.norm(ref_out)
+    M = OD.spectrum(ref_out)[0] + delta
+    assert got[0] == r
+    for i, k in ((1, 2), (2, 4), (3, 6)):
+        assert abs(got[i] - want[i]) <= k * M ** (k - 1) * math.sqrt(r) * delta, (k, got[i], want[i])
+
+
+@pytest.mark.parametrize("dt", ["bf16", "fp32"])
+def test_spectral_moments_closed_form(cuda, dt):
+    """Matrices U diag(s) V^T with known s (several shapes in one call, a zero
+    matrix among them): the library's moments against sum s^k, and its
+    orthogonality residual against RMS(s^2 - 1)."""
+    rng = np.random.default_rng([55, dt == "fp32"])
+    mats, want = [], []
+    for h, w in [(64, 96), (300, 130), (1, 40), (513, 512), (2048, 640)]:
+        k = min(h, w)
+        U, _ = np.linalg.qr(rng.standard_normal((h, k)))
+        V, _ = np.linalg.qr(rng.standard_normal((w, k)))
+        s = rng.uniform(0.3, 1.7, k)
+        x = workloads.round_to((U * s) @ V.T, dt)
+        mats.append(x.to(cuda))
+        want.append(OD.spectral_moments(x.double().numpy()))   # of the rounded matrix
+    mats.append(torch.zeros((40, 70), dtype=mats[0].dtype, device=cuda))
+    want.append((40, 0.0, 0.0, 0.0))
+    got = GD.spectral_moments(mats)
+    for g_, w_ in zip(got, want):
+        say(f"moments r={w_[0]}: {g_[1]:.6g} {g_[2]:.6g} {g_[3]:.6g} (want {w_[1]:.6g} {w_[2]:.6g} {w_[3]:.6g})")
+        assert g_[0] == w_[0]
+        for i in (1, 2, 3):
+            assert abs(g_[i] - w_[i]) <= 1e-5 * max(w_[i], 1e-30)
+        assert GD.orthogonality_residual(g_) == pytest.approx(OD.orthogonality_residual(w_), rel=1e-3, abs=1e-6)

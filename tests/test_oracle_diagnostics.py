@@ -96,6 +96,29 @@ def test_spectrum_closed_form(shape, coeffs):
     assert np.allclose(got, want, rtol=0, atol=1e-12)
 
 
+@pytest.mark.parametrize("shape", [(48, 80), (90, 36), (1, 7), (33, 33)])
+def test_spectral_moments_trace_identities(shape):
+    """The moments from the spectrum against traces of the Gram matrix of the
+    shorter side, G: sum s^2 = tr G, sum s^4 = ||G||_F^2, sum s^6 = tr G^3;
+    and the orthogonality residual of a matrix with known singular values."""
+    g = rng(8)
+    X = g.standard_normal(shape)
+    G = X @ X.T if shape[0] <= shape[1] else X.T @ X
+    r, m2, m4, m6 = D.spectral_moments(X)
+    assert r == min(shape)
+    assert m2 == pytest.approx(np.trace(G), rel=1e-12)
+    assert m4 == pytest.approx(np.sum(G * G), rel=1e-12)
+    assert m6 == pytest.approx(np.trace(G @ G @ G), rel=1e-12)
+    h, w = shape
+    k = min(h, w)
+    U, _ = np.linalg.qr(g.standard_normal((h, k)))
+    V, _ = np.linalg.qr(g.standard_normal((w, k)))
+    s = g.uniform(0.5, 1.5, k)
+    want = math.sqrt(np.mean((s ** 2 - 1.0) ** 2))
+    assert D.orthogonality_residual(D.spectral_moments((U * s) @ V.T)) == pytest.approx(want, rel=1e-9, abs=1e-12)
+    assert D.orthogonality_residual(D.spectral_moments(U @ V.T)) < 1e-7
+
+
 def test_block_diagonal_distance_closed_form():
     """M = diag(B1, B2) with B1, B2 whole T x T tiles of equal Frobenius norm r.
     The off-diagonal tiles are zero and stay zero; each diagonal tile is
