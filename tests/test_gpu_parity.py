@@ -274,7 +274,7 @@ def test_deterministic_and_tile_independent(cuda, dt, T):
     assert torch.isnan(c[mask]).all()
 
 
-@pytest.mark.parametrize("dt,T", [("bf16", 64), ("bf16", 256), ("fp32", 128)])
+@pytest.mark.parametrize("dt,T", [("bf16", 64), ("bf16", 256), ("fp32", 64), ("fp32", 128)])
 def test_transposed_view_and_batch(cuda, dt, T):
     rng = np.random.default_rng([16, T])
     xs = [workloads.round_to(rng.standard_normal(s), dt).cuda() for s in [(300, 170), (170, 300), (64, 64)]]
