@@ -50,11 +50,12 @@
 // symmetric) for both; Y'^T = Y^T B takes AL(Y), read from LDS with
 // ds_read_tr16_b64, and AL(B), and lands in RL(Y').
 //
-// Measured on MI355X (24 transformer layers, 1.2 M tiles, K = 5): 1.66 ms per
+// Measured on MI355X (24 transformer layers, 1.2 M tiles, K = 5): 1.65 ms per
 // call.  Steps: 2.46 ms with every step in fp32 and one workgroup per tile;
 // 2.00 ms with the hi/lo fp32 step, the tile pairing below (HBM reads
 // halved) and four waves per SIMD; 1.72 ms with the nested fp32 step and the
-// two step loops; 1.66 ms with five waves per SIMD (at most 96 registers).
+// two step loops; 1.66 ms with five waves per SIMD (at most 96 registers);
+// 1.65 ms with the sum of squares taken from the unpacked row fragments.
 // Six waves would spill.  Loading the next tile during the current one was
 // slower both into registers (5-8 %) and straight into LDS with
 // global_load_lds (7 %).  LDS row strides of 48 and 56 elements were 1-2 %
@@ -190,32 +191,30 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(MUON ? 4 : 5
                 chunk[it] = v;
             }
         }
-        float ss = 0.f;
 #pragma unroll
         for (int it = 0; it < IO::NCH; ++it)
+            *reinterpret_cast<u16x8*>(&sX[(crow + 16 * it) * kLD32 + ccol]) = chunk[it];
+        __syncthreads();
+        // Ym: the iterate in fp32 (RL), read back once; the sum of squares is
+        // taken from the same values (the lanes' row fragments cover the tile
+        // once), so the bf16 values are unpacked only here
+        f32x16 Ym;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float x = bf2f(chunk[it][e]);
-                ss = __builtin_fmaf(x, x, ss);
-            }
+        for (int m = 0; m < 4; ++m) {
+            const u16x4 v = *reinterpret_cast<const u16x4*>(&sX[rl_off(m)]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Ym[4 * m + e] = bf2f(v[e]);
+        }
+        float ss = 0.f;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) ss = __builtin_fmaf(Ym[q], Ym[q], ss);
         ss = wave_sum_dpp(ss);
         // v_sqrt_f32 and v_rcp_f32 (1 ulp each): the scale is a per-tile
         // constant whose relative error of a few 1e-7 is far below the bf16
         // rounding
         const float scale =
             (args.normalize ? __builtin_amdgcn_rcpf(__builtin_amdgcn_sqrtf(ss) + args.eps) : 1.0f) * cs.g0;
-#pragma unroll
-        for (int it = 0; it < IO::NCH; ++it)
-            *reinterpret_cast<u16x8*>(&sX[(crow + 16 * it) * kLD32 + ccol]) = chunk[it];
-        __syncthreads();
-        // Ym: the iterate in fp32 (RL); XR: its bf16 operand (RL)
-        f32x16 Ym;
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const u16x4 v = *reinterpret_cast<const u16x4*>(&sX[rl_off(m)]);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) Ym[4 * m + e] = bf2f(v[e]) * scale;
-        }
+        Ym = Ym * scale;
         u32x4 XR[2];
         __syncthreads();
         // fp32 step (k < n_master): with Ab = bf16(kappa A_Y) and s = +-1,
