@@ -159,6 +159,7 @@ KERNEL_SOURCES = {
     "resident32_kernel": ["resident32.hip", "device_util.h", "common.h"],
     "resident_kernel<64>": ["resident.hip", "device_util.h", "common.h"],
     "resident_kernel<128>": ["resident.hip", "device_util.h", "common.h"],
+    "resident_f32_kernel": ["resident_f32.hip", "common.h"],
     "resident256_kernel": ["resident256.hip", "device_util.h", "common.h"],
     "pair_stats": ["pair_stats.hip", "pair_stats.h"],
 }
@@ -217,7 +218,7 @@ def dominant_kernel_roofline(H, torch, mats, shapes, T, K, plan, stream, ms_per_
     dsize = 2 if w.dtype == "bf16" else 4
     nbytes = 2.0 * dsize * sum(h * ww for h, ww in shapes)
     kernel_tile = plan["kernel_tile"]
-    main = KERNEL_OF_TILE.get(kernel_tile)
+    main = "resident_f32_kernel" if w.dtype == "fp32" and kernel_tile == 64 else KERNEL_OF_TILE.get(kernel_tile)
     one_launch = plan["chunks"] == 0 and plan["resident_launches"] == 1
     if one_launch and plan["tail_tiles"] == 0 and main:
         kernel, tiles, ms, flops = main, plan["tiles"], ms_per_step, alg

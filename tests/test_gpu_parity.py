@@ -181,19 +181,21 @@ def test_eps_argument(cuda, eps):
 STEPS16 = [COEFFS] * 5 + [(1.5, -0.5, 0.0)] * 11
 
 
-@pytest.mark.parametrize("shape,T", [((300, 260), 128), ((300, 200), 256), ((600, 520), 512), ((130, 40), 64),
-                                     ((300, 260), 32)])
-def test_max_steps(cuda, shape, T):
+@pytest.mark.parametrize("shape,T,dt", [((300, 260), 128, "bf16"), ((300, 200), 256, "bf16"),
+                                        ((600, 520), 512, "bf16"), ((130, 40), 64, "bf16"), ((300, 260), 32, "bf16"),
+                                        ((300, 260), 64, "fp32"), ((300, 260), 128, "fp32")])
+def test_max_steps(cuda, shape, T, dt):
     """K = 16, the largest step count, on every route (kernel tiles 32, 128
-    and 256, the step path with bf16 and fp32 workspaces, split precision):
-    five quintic steps, then eleven cubic ones (1.5, -0.5, 0), on a few tiles.
-    Over many tiles the bf16 iterate of kernel tiles 64 and up exceeds the
-    bound on a tail of them (test_gpu_precision.py pins that)."""
+    and 256, the step path with bf16 and fp32 workspaces, split precision,
+    fp32 tiles on chip and on the step path): five quintic steps, then eleven
+    cubic ones (1.5, -0.5, 0), on a few tiles.  Over many tiles the bf16
+    iterate of kernel tiles 64 and up exceeds the bound on a tail of them
+    (test_gpu_precision.py pins that)."""
     rng = np.random.default_rng([37, T])
-    x = workloads.round_to(rng.standard_normal(shape), "bf16")
-    err, _ = full_check(x, T, "bf16", K=16, abc=STEPS16)
-    say(f"K=16 {shape} T={T}: {err:.3e}")
-    assert err <= TOL["bf16"]
+    x = workloads.round_to(rng.standard_normal(shape), dt)
+    err, _ = full_check(x, T, dt, K=16, abc=STEPS16)
+    say(f"K=16 {dt} {shape} T={T}: {err:.3e}")
+    assert err <= TOL[dt]
 
 
 # steps with c = 0 (the cubic iteration) mixed with quintic ones
