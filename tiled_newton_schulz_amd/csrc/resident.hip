@@ -72,11 +72,11 @@ void resident_kernel(const ResidentArgs args) {
     // storing) at the same time.
     constexpr bool PERSIST = TK == 128 && !MUON && !PRECISE;
     // Kernel tile 128 folds the normalisation into the first step (K > 0):
-    // the raw tile goes to LDS, the sum of squares is taken from the row
-    // fragments of the first A product, and that step rounds s^2 A (the A of
-    // the scaled tile) and scales the coefficients of B' by s, so that it
-    // applies s B'(s^2 A) to the raw tile.  The eight-wave kernel does the
-    // same, operation for operation.
+    // the raw tile goes to LDS, the sum of squares is the trace of the first
+    // A product (its diagonal blocks are computed first), and that step
+    // rounds s^2 A (the A of the scaled tile) and scales the coefficients of
+    // B' by s, so that it applies s B'(s^2 A) to the raw tile.  The eight-wave
+    // kernel does the same, operation for operation.
     constexpr bool FOLD = TK == 128;
     using FIRSTC = std::bool_constant<FOLD>;
 
@@ -314,27 +314,36 @@ void resident_kernel(const ResidentArgs args) {
                 for (int kc = 0; kc < NK; ++kc)
                     RF[I][kc] = *reinterpret_cast<const u32x4*>(&sX[(I * 32 + l32) * LD + kc * 16 + g * 8]);
             if constexpr (FIRST) {
-                // sum of squares of the raw tile, in row-fragment order
-                float sq = 0.f;
+                // The sum of squares of the raw tile is the trace of its Gram
+                // matrix: the diagonal blocks come first, and each lane adds
+                // its diagonal elements of the NB blocks in block order, then
+                // the wave sums (the eight-wave kernel forms the same sums).
+                f32x16 dacc[NB];
 #pragma unroll
-                for (int I = 0; I < NB; ++I)
+                for (int I = 0; I < NB; ++I) {
+                    dacc[I] = f32x16{};
 #pragma unroll
-                    for (int kc = 0; kc < NK; ++kc)
+                    for (int kc = 0; kc < NK; ++kc) dacc[I] = mfma32w(RF[I][kc], RF[I][kc], dacc[I]);
+                }
+                f32x16 dsum = dacc[0];
 #pragma unroll
-                        for (int k = 0; k < 4; ++k) {
-                            const float x0 = lo_f(RF[I][kc][k]), x1 = hi_f(RF[I][kc][k]);
-                            sq = __builtin_fmaf(x0, x0, sq);
-                            sq = __builtin_fmaf(x1, x1, sq);
-                        }
-                sq = wave_sum(sq);
+                for (int I = 1; I < NB; ++I) dsum = dsum + dacc[I];
+                const float sq = wave_sum(diag_pick(dsum, l32, g));
                 const float sc = args.normalize ? 1.0f / (sqrtf(sq) + args.eps) : 1.0f;
                 s2 = sc * sc;
                 ca *= sc;
                 cb *= sc;
                 cc *= sc;
+#pragma unroll
+                for (int I = 0; I < NB; ++I) {
+                    const f32x16 a = dacc[I] * s2;
+                    Abf[I][I][0] = cvt8(a, 0);
+                    Abf[I][I][1] = cvt8(a, 8);
+                }
             }
-            // lower blocks (I >= J), two accumulator chains at a time
-            constexpr int NL = NB * (NB + 1) / 2;
+            // lower blocks (I >= J), two accumulator chains at a time (the
+            // first folded step has done the diagonal ones)
+            constexpr int NL = FIRST ? NB * (NB - 1) / 2 : NB * (NB + 1) / 2;
 #pragma unroll
             for (int p = 0; p < NL; p += 2) {
                 int I1 = 0, J1 = 0, I2 = 0, J2 = 0;
@@ -344,6 +353,7 @@ void resident_kernel(const ResidentArgs args) {
                     for (int i = 0; i < NB; ++i)
 #pragma unroll
                         for (int j = 0; j <= i; ++j) {
+                            if (FIRST && j == i) continue;
                             if (c == p) { I1 = i; J1 = j; }
                             if (c == p + 1) { I2 = i; J2 = j; }
                             ++c;
@@ -720,6 +730,7 @@ __global__ __launch_bounds__(512) void resident_coop_kernel(const ResidentArgs a
     __shared__ __attribute__((aligned(16))) unsigned short sX[TK * LD];
     __shared__ __attribute__((aligned(16))) u32x4 sF[NB * NB * 2 * 64];   // AL fragments, lane-major
     __shared__ float red[1];
+    __shared__ float sDiag[NB * 64];   // diagonal elements of the first A, per block and lane
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -763,10 +774,10 @@ __global__ __launch_bounds__(512) void resident_coop_kernel(const ResidentArgs a
     }
     __syncthreads();
     // Sum of squares in the one-wave kernel's order.  With K > 0 the
-    // normalisation is folded into the first step there: the sum is taken in
-    // row-fragment order (lane l sums rows l % 32 + 32 I, columns
-    // 16 kc + 8 (l / 32) .. + 7) once the first step's A products are issued.
-    // With K = 0 it is taken here (lane l sums chunks l, l + 64, ...).
+    // normalisation is folded into the first step there: the sum is the trace
+    // of the raw tile's Gram matrix, taken from the diagonal blocks of the
+    // first A product.  With K = 0 it is taken here (lane l sums chunks l,
+    // l + 64, ...).
     const bool fold = args.K > 0;
     float scale = 1.0f;
     if (!fold) {
@@ -839,26 +850,17 @@ __global__ __launch_bounds__(512) void resident_coop_kernel(const ResidentArgs a
                 }
             }
             if (first) {
-                if (w == 0) {
-                    float ss = 0.f;
+                // the trace of the raw Gram matrix, summed as in the one-wave
+                // kernel: per lane its diagonal elements of blocks 0 .. 3 in
+                // order, then over the wave
 #pragma unroll
-                    for (int I = 0; I < NB; ++I)
-#pragma unroll
-                        for (int kc = 0; kc < NK; ++kc) {
-                            const u32x4 v =
-                                *reinterpret_cast<const u32x4*>(&sX[(I * 32 + l32) * LD + kc * 16 + g * 8]);
-#pragma unroll
-                            for (int k = 0; k < 4; ++k) {
-                                const float x0 = lo_f(v[k]), x1 = hi_f(v[k]);
-                                ss = __builtin_fmaf(x0, x0, ss);
-                                ss = __builtin_fmaf(x1, x1, ss);
-                            }
-                        }
-                    ss = wave_sum(ss);
-                    if (lane == 0) red[0] = ss;
-                }
+                for (int i = 0; i < 2; ++i)
+                    if (2 * h + i == c) sDiag[c * 64 + lane] = diag_pick(acc[i], l32, g);
                 __syncthreads();
-                scale = args.normalize ? 1.0f / (sqrtf(red[0]) + args.eps) : 1.0f;
+                float t = sDiag[lane];
+#pragma unroll
+                for (int I = 1; I < NB; ++I) t = t + sDiag[I * 64 + lane];
+                scale = args.normalize ? 1.0f / (sqrtf(wave_sum(t)) + args.eps) : 1.0f;
                 const float s2 = scale * scale;
                 ca *= scale;
                 cb *= scale;
