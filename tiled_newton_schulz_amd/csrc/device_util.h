@@ -63,15 +63,6 @@ __device__ __forceinline__ f32x16 mfma32w(u32x4 a, u32x4 b, f32x16 c) {
 __device__ __forceinline__ float diag_term(int q, int l32, int g, float ca) {
     return ((q >> 2) * 8 + g * 4 + (q & 3) == l32) ? ca : 0.f;
 }
-// The diagonal element of an AL block held by this lane (lanes with g equal
-// to bit 2 of l % 32 hold one, at q = (l32 / 8) 4 + l32 % 4), else +0.
-__device__ __forceinline__ float diag_pick(const f32x16& v, int l32, int g) {
-    float r = 0.f;
-#pragma unroll
-    for (int q = 0; q < 16; ++q)
-        if ((q >> 2) * 8 + g * 4 + (q & 3) == l32) r = v[q];
-    return r;
-}
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

@@ -49,6 +49,18 @@
 
 namespace himuon {
 
+namespace {
+// The diagonal element of an AL block held by this lane (lanes with g equal
+// to bit 2 of l % 32 hold one, at q = (l32 / 8) 4 + l32 % 4), else +0.
+__device__ __forceinline__ float diag_pick(const f32x16& v, int l32, int g) {
+    float r = 0.f;
+#pragma unroll
+    for (int q = 0; q < 16; ++q)
+        if ((q >> 2) * 8 + g * 4 + (q & 3) == l32) r = v[q];
+    return r;
+}
+}  // namespace
+
 template <int TK, bool MUON, bool PRECISE>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(TK == 64 && !PRECISE ? 4 : 1)))
 void resident_kernel(const ResidentArgs args) {
