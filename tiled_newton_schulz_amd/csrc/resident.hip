@@ -700,17 +700,46 @@ void resident_kernel(const ResidentArgs args) {
             old = me.w_ld;
             ovec = vec_ok(me.w, me.w_ld, c0);
         }
+        if (h == TK && w == TK && ovec) {
+            // a whole aligned tile: every lane address is one base plus a
+            // constant row stride, and the LDS reads of a batch of chunks are
+            // issued together, so the stores wait on one LDS round trip per
+            // batch rather than one per chunk
+            constexpr int RPI = 64 / IO::CPR;   // rows per chunk round
+            constexpr int BT = IO::NCH < 8 ? IO::NCH : 8;
+            unsigned short* p0 = obase + (int64_t)(lane / IO::CPR) * old + (lane % IO::CPR) * 8;
+            const unsigned short* q0 = &sX[(lane / IO::CPR) * LD + (lane % IO::CPR) * 8];
 #pragma unroll
-        for (int it = 0; it < IO::NCH; ++it) {
-            const int idx = it * 64 + lane;
-            const int r = idx / IO::CPR, col = (idx % IO::CPR) * 8;
-            u16x8 v = *reinterpret_cast<const u16x8*>(&sX[r * LD + col]);
-            if constexpr (MUON) {
-                u16x8 wv = IO::load(obase, old, r, col, h, w, ovec);
+            for (int it0 = 0; it0 < IO::NCH; it0 += BT) {
+                u16x8 v[BT];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) v[e] = f2bf(bf2f(wv[e]) - args.eta * bf2f(v[e]));
+                for (int u = 0; u < BT; ++u) v[u] = *reinterpret_cast<const u16x8*>(q0 + (it0 + u) * RPI * LD);
+                if constexpr (MUON) {
+                    u16x8 wv[BT];
+#pragma unroll
+                    for (int u = 0; u < BT; ++u)
+                        wv[u] = *reinterpret_cast<const u16x8*>(p0 + (int64_t)((it0 + u) * RPI) * old);
+#pragma unroll
+                    for (int u = 0; u < BT; ++u)
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) v[u][e] = f2bf(bf2f(wv[u][e]) - args.eta * bf2f(v[u][e]));
+                }
+#pragma unroll
+                for (int u = 0; u < BT; ++u) *reinterpret_cast<u16x8*>(p0 + (int64_t)((it0 + u) * RPI) * old) = v[u];
             }
-            IO::store(obase, old, r, col, h, w, ovec, v);
+        } else {
+#pragma unroll
+            for (int it = 0; it < IO::NCH; ++it) {
+                const int idx = it * 64 + lane;
+                const int r = idx / IO::CPR, col = (idx % IO::CPR) * 8;
+                u16x8 v = *reinterpret_cast<const u16x8*>(&sX[r * LD + col]);
+                if constexpr (MUON) {
+                    u16x8 wv = IO::load(obase, old, r, col, h, w, ovec);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) v[e] = f2bf(bf2f(wv[e]) - args.eta * bf2f(v[e]));
+                }
+                IO::store(obase, old, r, col, h, w, ovec, v);
+            }
         }
     }
     if (!next) break;
