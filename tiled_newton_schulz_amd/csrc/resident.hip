@@ -810,7 +810,13 @@ __global__ __launch_bounds__(512) void resident_coop_kernel(const ResidentArgs a
                 IO::store(mbase, me.m_ld, r, col, hh, wd, mvec, v);
             }
             chunk[it] = v;
-            *reinterpret_cast<u16x8*>(&sX[r * LD + col]) = v;
+        }
+        // all loads in flight before the first LDS write waits for one
+#pragma unroll
+        for (int it = 0; it < NCH; ++it) {
+            const int idx = it * 512 + tid;
+            const int r = idx / IO::CPR, col = (idx % IO::CPR) * 8;
+            *reinterpret_cast<u16x8*>(&sX[r * LD + col]) = chunk[it];
         }
     }
     __syncthreads();
@@ -991,11 +997,19 @@ __global__ __launch_bounds__(512) void resident_coop_kernel(const ResidentArgs a
         old = me.w_ld;
         ovec = vec_ok(me.w, me.w_ld, tg.c0);
     }
+    // the LDS reads of all the thread's chunks first, then the stores
+    u16x8 out[NCH];
 #pragma unroll
     for (int it = 0; it < NCH; ++it) {
         const int idx = it * 512 + tid;
         const int r = idx / IO::CPR, col = (idx % IO::CPR) * 8;
-        u16x8 v = *reinterpret_cast<const u16x8*>(&sX[r * LD + col]);
+        out[it] = *reinterpret_cast<const u16x8*>(&sX[r * LD + col]);
+    }
+#pragma unroll
+    for (int it = 0; it < NCH; ++it) {
+        const int idx = it * 512 + tid;
+        const int r = idx / IO::CPR, col = (idx % IO::CPR) * 8;
+        u16x8 v = out[it];
         if constexpr (MUON) {
             u16x8 wv = IO::load(obase, old, r, col, hh, wd, ovec);
 #pragma unroll
