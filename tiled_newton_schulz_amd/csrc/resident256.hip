@@ -207,16 +207,19 @@ __global__ __launch_bounds__(512) void resident256_kernel(const ResidentArgs arg
     constexpr int NCH = XR * 32 / 512;
     const int cpr = tr ? 16 : 32;
 
-    // ---- load (Muon: M <- mu M + G, stored) into LDS, sum of squares ----
+    // ---- load (Muon: M <- mu M + G, stored), sum of squares, scaled tile
+    //      into LDS.  Every load of the thread is issued before the first one
+    //      is waited for, and the tile stays in registers until the scale is
+    //      known, so it is written to LDS once. ----
     {
-        float ss = 0.f;
         const unsigned short* gbase = nullptr;
         bool gvec = false;
         if constexpr (MUON) {
             gbase = reinterpret_cast<const unsigned short*>(me.g) + (int64_t)tg.r0 * me.g_ld + tg.c0;
             gvec = vec_ok(me.g, me.g_ld, tg.c0);
         }
-#pragma unroll 4
+        u16x8 chunk[NCH];
+#pragma unroll
         for (int it = 0; it < NCH; ++it) {
             const int idx = it * 512 + tid;
             const int r = idx / cpr, col = (idx % cpr) * 8;
@@ -227,15 +230,13 @@ __global__ __launch_bounds__(512) void resident256_kernel(const ResidentArgs arg
                 for (int e = 0; e < 8; ++e) v[e] = f2bf(args.mu * bf2f(v[e]) + bf2f(gv[e]));
                 IO::store(mbase, me.m_ld, r, col, h, wd, mvec, v);
             }
-#pragma unroll
-            for (int e = 0; e < 8; ++e) { const float x = bf2f(v[e]); ss = __builtin_fmaf(x, x, ss); }
-            if (!tr) {
-                *reinterpret_cast<u16x8*>(&sX[r * kLD + col]) = v;
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) sX[(col + e) * kLD + r] = v[e];
-            }
+            chunk[it] = v;
         }
+        float ss = 0.f;
+#pragma unroll
+        for (int it = 0; it < NCH; ++it)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) { const float x = bf2f(chunk[it][e]); ss = __builtin_fmaf(x, x, ss); }
         ss = wave_sum(ss);
         if (lane == 0) red[w] = ss;
         __syncthreads();
@@ -243,14 +244,19 @@ __global__ __launch_bounds__(512) void resident256_kernel(const ResidentArgs arg
 #pragma unroll
         for (int i = 0; i < 8; ++i) tot += red[i];
         const float scale = args.normalize ? 1.0f / (sqrtf(tot) + args.eps) : 1.0f;
-#pragma unroll 4
+#pragma unroll
         for (int it = 0; it < NCH; ++it) {
             const int idx = it * 512 + tid;
-            const int r = idx >> 5, col = (idx & 31) * 8;
-            u16x8 v = *reinterpret_cast<const u16x8*>(&sX[r * kLD + col]);
+            const int r = idx / cpr, col = (idx % cpr) * 8;
+            u16x8 v;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = f2bf(bf2f(v[e]) * scale);
-            *reinterpret_cast<u16x8*>(&sX[r * kLD + col]) = v;
+            for (int e = 0; e < 8; ++e) v[e] = f2bf(bf2f(chunk[it][e]) * scale);
+            if (!tr) {
+                *reinterpret_cast<u16x8*>(&sX[r * kLD + col]) = v;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) sX[(col + e) * kLD + r] = v[e];
+            }
         }
         __syncthreads();
     }
