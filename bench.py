@@ -332,6 +332,65 @@ def gram_flops(shapes, K, restart):
     return tot
 
 
+def muon_bench(H, torch, w, mats, T, K, steps, warmup, warmup_seconds, cap):
+    """Time himuon_muon_step (M <- mu M + G, W <- W - eta tiledNS(M), fused)
+    on the workload's matrices as M, with seeded G and W of the same shapes.
+    The flops are the tiled map's; the HBM bytes are five passes over the
+    elements (M, G and W read, M and W written).  M and W change from call to
+    call, as they would over optimiser steps."""
+    import workloads
+    shapes = [tuple(m.shape) for m in mats]
+    gen = torch.Generator(device=mats[0].device).manual_seed(12345)
+    G = [(torch.randn(sh, device=mats[0].device, generator=gen) * 0.01).to(mats[0].dtype) for sh in shapes]
+    W = [(torch.randn(sh, device=mats[0].device, generator=gen) * 0.02).to(mats[0].dtype) for sh in shapes]
+    full, _ = H.himuon_workspace_size(mats, T)
+    ws_bytes = (min(full, cap) if cap else full) if full else 0
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=mats[0].device) if ws_bytes else None
+    stream = torch.cuda.current_stream()
+
+    def step():
+        H.himuon_muon_step(W, mats, G, T, K, workloads.COEFFS, workspace=ws, workspace_bytes=ws_bytes,
+                           stream=stream)
+
+    t0 = time.perf_counter()
+    n_warm = 0
+    while n_warm < warmup or time.perf_counter() - t0 < warmup_seconds:
+        step()
+        n_warm += 1
+        if n_warm % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / steps
+    alg = algorithmic_flops(shapes, T, K)
+    nominal = sum(6.0 * h * ww * T * K for h, ww in shapes)
+    es = 2 if w.dtype == "bf16" else 4
+    io_bytes = 5.0 * sum(h * ww for h, ww in shapes) * es
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
+    achieved = alg / (ms * 1e-3) / 1e12
+    return {
+        "metric": "fused Muon step (M <- mu M + G, W <- W - eta tiledNS(M)) TFLOP/s (6*H*W*T*K)",
+        "value": round(nominal / (ms * 1e-3) / 1e12, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": steps,
+        "warmup": warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic (seeded normal M, G and W)",
+        "config": {"workload": w.name, "matrices": len(shapes), "T": T, "K": K, "mu": 0.95, "eta": 0.02,
+                   "elements": sum(h * ww for h, ww in shapes), "workspace_bytes": ws_bytes,
+                   "parallelism": "single GPU"},
+        "pct_bf16_peak": round(100.0 * achieved / PEAK_BF16_TFLOPS, 2),
+        "hbm_gbs_io": round(io_bytes / (ms * 1e-3) / 1e9, 1),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4), "traffic": None, "kernel": "whole step",
+                     "hbm_floor_ms": round(io_bytes / 8e12 * 1e3, 4)},
+        "warmup_steps_run": n_warm,
+    }
+
+
 def gram_bench(H, torch, w, mats, K, restart, steps, warmup, cap, no_cpu):
     """Time himuon_gram_ns (the full-matrix map through the Gram iteration)
     against himuon_tiled_ns with T = max(rows, cols) (the standard full map)
@@ -438,6 +497,8 @@ def main():
                     help="time the full-matrix map through the Gram iteration (himuon_gram_ns) against the "
                          "standard full map instead of the tiled map")
     ap.add_argument("--restart", type=int, default=2, help="Gram iteration restart point (0: none)")
+    ap.add_argument("--muon", action="store_true",
+                    help="time the fused Muon step (himuon_muon_step) on the workload instead of the map")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB, 5 times (used to "
                          "calibrate the HBM byte counters)")
@@ -450,7 +511,7 @@ def main():
 
     # the CPU oracle first, before anything touches the GPU
     cpu = None
-    if not (args.no_cpu or args.schedule or args.pair_stats or args.gram or args.copy_mib):
+    if not (args.no_cpu or args.schedule or args.pair_stats or args.gram or args.muon or args.copy_mib):
         import workloads
         wl = workloads.WORKLOADS[args.workload]
         cpu = cpu_baseline(wl, args.T or wl.T, args.K)
@@ -487,6 +548,10 @@ def main():
     if args.gram:
         print(json.dumps(gram_bench(H, torch, w, mats, args.K, args.restart, args.steps, args.warmup, cap,
                                     args.no_cpu)), flush=True)
+        return
+    if args.muon:
+        print(json.dumps(muon_bench(H, torch, w, mats, T, K, args.steps, args.warmup, args.warmup_seconds, cap)),
+              flush=True)
         return
     full, mn = H.himuon_workspace_size(mats, T)
     ws = None

@@ -108,6 +108,56 @@ __device__ __forceinline__ bool vec_ok(const void* base, int64_t ld, int c0) {
     return ((reinterpret_cast<uintptr_t>(base) & 15) == 0) && ((ld & 7) == 0) && ((c0 & 7) == 0);
 }
 
+// Muon prologue M <- mu M + G (rounded to bf16, stored) over NCH 16-byte
+// chunks of a whole, aligned tile: chunk it of this thread sits it * mstride
+// (M) and it * gstride (G) elements past pm and pg.  The loads of a batch of BT
+// chunks of M and of G are all issued before any is waited for (one chunk at
+// a time, each store would hold back the next chunk's loads); the new M is
+// returned in chunk.
+template <int NCH, int BT>
+__device__ __forceinline__ void muon_prologue_whole(unsigned short* pm, int64_t mstride, const unsigned short* pg,
+                                                    int64_t gstride, float mu, u16x8 (&chunk)[NCH]) {
+    static_assert(NCH % BT == 0, "whole batches");
+#pragma unroll
+    for (int it0 = 0; it0 < NCH; it0 += BT) {
+        u16x8 mv[BT], gv[BT];
+#pragma unroll
+        for (int u = 0; u < BT; ++u) mv[u] = *reinterpret_cast<const u16x8*>(pm + (it0 + u) * mstride);
+#pragma unroll
+        for (int u = 0; u < BT; ++u) gv[u] = *reinterpret_cast<const u16x8*>(pg + (it0 + u) * gstride);
+#pragma unroll
+        for (int u = 0; u < BT; ++u) {
+            u16x8 v;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = f2bf(mu * bf2f(mv[u][e]) + bf2f(gv[u][e]));
+            chunk[it0 + u] = v;
+            *reinterpret_cast<u16x8*>(pm + (it0 + u) * mstride) = v;
+        }
+    }
+}
+
+// Muon update W <- W - eta X (X rounded to bf16 first, as stored) over NCH
+// chunks of a whole, aligned tile laid out as in muon_prologue_whole, the W
+// loads of a batch of BT chunks issued together.
+template <int NCH, int BT>
+__device__ __forceinline__ void muon_update_whole(unsigned short* pw, int64_t wstride, float eta,
+                                                  const u16x8 (&x)[NCH]) {
+    static_assert(NCH % BT == 0, "whole batches");
+#pragma unroll
+    for (int it0 = 0; it0 < NCH; it0 += BT) {
+        u16x8 wv[BT];
+#pragma unroll
+        for (int u = 0; u < BT; ++u) wv[u] = *reinterpret_cast<const u16x8*>(pw + (it0 + u) * wstride);
+#pragma unroll
+        for (int u = 0; u < BT; ++u) {
+            u16x8 v;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = f2bf(bf2f(wv[u][e]) - eta * bf2f(x[it0 + u][e]));
+            *reinterpret_cast<u16x8*>(pw + (it0 + u) * wstride) = v;
+        }
+    }
+}
+
 }  // namespace
 
 }  // namespace himuon

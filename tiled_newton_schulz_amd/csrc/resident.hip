@@ -135,7 +135,13 @@ void resident_kernel(const ResidentArgs args) {
             gbase = reinterpret_cast<const unsigned short*>(me.g) + (int64_t)r0 * me.g_ld + c0;
             gvec = vec_ok(me.g, me.g_ld, c0);
         }
-        if (!PERSIST || !loaded) {
+        if (MUON && h == TK && w == TK && mvec && gvec) {
+            constexpr int RPI = 64 / IO::CPR;   // rows per chunk round
+            muon_prologue_whole<IO::NCH, (IO::NCH < 8 ? IO::NCH : 8)>(
+                mbase + (int64_t)(lane / IO::CPR) * me.m_ld + (lane % IO::CPR) * 8, (int64_t)RPI * me.m_ld,
+                gbase + (int64_t)(lane / IO::CPR) * me.g_ld + (lane % IO::CPR) * 8, (int64_t)RPI * me.g_ld, args.mu,
+                chunk);
+        } else if (!PERSIST || !loaded) {
 #pragma unroll
             for (int it = 0; it < IO::NCH; ++it) {
                 const int idx = it * 64 + lane;
@@ -798,18 +804,26 @@ __global__ __launch_bounds__(512) void resident_coop_kernel(const ResidentArgs a
             gbase = reinterpret_cast<const unsigned short*>(me.g) + (int64_t)tg.r0 * me.g_ld + tg.c0;
             gvec = vec_ok(me.g, me.g_ld, tg.c0);
         }
+        if (MUON && hh == TK && wd == TK && mvec && gvec) {
+            constexpr int RPI = 512 / IO::CPR;   // rows per chunk round
+            muon_prologue_whole<NCH, NCH>(mbase + (int64_t)(tid / IO::CPR) * me.m_ld + (tid % IO::CPR) * 8,
+                                          (int64_t)RPI * me.m_ld,
+                                          gbase + (int64_t)(tid / IO::CPR) * me.g_ld + (tid % IO::CPR) * 8,
+                                          (int64_t)RPI * me.g_ld, args.mu, chunk);
+        } else {
 #pragma unroll
-        for (int it = 0; it < NCH; ++it) {
-            const int idx = it * 512 + tid;
-            const int r = idx / IO::CPR, col = (idx % IO::CPR) * 8;
-            u16x8 v = IO::load(mbase, me.m_ld, r, col, hh, wd, mvec);
-            if constexpr (MUON) {
-                u16x8 gv = IO::load(gbase, me.g_ld, r, col, hh, wd, gvec);
+            for (int it = 0; it < NCH; ++it) {
+                const int idx = it * 512 + tid;
+                const int r = idx / IO::CPR, col = (idx % IO::CPR) * 8;
+                u16x8 v = IO::load(mbase, me.m_ld, r, col, hh, wd, mvec);
+                if constexpr (MUON) {
+                    u16x8 gv = IO::load(gbase, me.g_ld, r, col, hh, wd, gvec);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) v[e] = f2bf(args.mu * bf2f(v[e]) + bf2f(gv[e]));
-                IO::store(mbase, me.m_ld, r, col, hh, wd, mvec, v);
+                    for (int e = 0; e < 8; ++e) v[e] = f2bf(args.mu * bf2f(v[e]) + bf2f(gv[e]));
+                    IO::store(mbase, me.m_ld, r, col, hh, wd, mvec, v);
+                }
+                chunk[it] = v;
             }
-            chunk[it] = v;
         }
         // all loads in flight before the first LDS write waits for one
 #pragma unroll
@@ -1004,6 +1018,12 @@ __global__ __launch_bounds__(512) void resident_coop_kernel(const ResidentArgs a
         const int idx = it * 512 + tid;
         const int r = idx / IO::CPR, col = (idx % IO::CPR) * 8;
         out[it] = *reinterpret_cast<const u16x8*>(&sX[r * LD + col]);
+    }
+    if (MUON && hh == TK && wd == TK && ovec) {
+        constexpr int RPI = 512 / IO::CPR;
+        muon_update_whole<NCH, NCH>(obase + (int64_t)(tid / IO::CPR) * old + (tid % IO::CPR) * 8, (int64_t)RPI * old,
+                                    args.eta, out);
+        return;
     }
 #pragma unroll
     for (int it = 0; it < NCH; ++it) {

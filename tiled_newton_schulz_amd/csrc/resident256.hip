@@ -219,18 +219,28 @@ __global__ __launch_bounds__(512) void resident256_kernel(const ResidentArgs arg
             gvec = vec_ok(me.g, me.g_ld, tg.c0);
         }
         u16x8 chunk[NCH];
+        // a whole tile in its own layout: XR rows of 256 (wide or square) or
+        // 256 rows of XR = 128 (tall)
+        if (MUON && (tr ? (h == kT && wd == XR) : (h == XR && wd == kT)) && mvec && gvec) {
+            const int rpi = 512 / cpr;   // rows per chunk round
+            muon_prologue_whole<NCH, 8>(mbase + (int64_t)(tid / cpr) * me.m_ld + (tid % cpr) * 8,
+                                        (int64_t)rpi * me.m_ld,
+                                        gbase + (int64_t)(tid / cpr) * me.g_ld + (tid % cpr) * 8,
+                                        (int64_t)rpi * me.g_ld, args.mu, chunk);
+        } else {
 #pragma unroll
-        for (int it = 0; it < NCH; ++it) {
-            const int idx = it * 512 + tid;
-            const int r = idx / cpr, col = (idx % cpr) * 8;
-            u16x8 v = IO::load(mbase, me.m_ld, r, col, h, wd, mvec);
-            if constexpr (MUON) {
-                u16x8 gv = IO::load(gbase, me.g_ld, r, col, h, wd, gvec);
+            for (int it = 0; it < NCH; ++it) {
+                const int idx = it * 512 + tid;
+                const int r = idx / cpr, col = (idx % cpr) * 8;
+                u16x8 v = IO::load(mbase, me.m_ld, r, col, h, wd, mvec);
+                if constexpr (MUON) {
+                    u16x8 gv = IO::load(gbase, me.g_ld, r, col, h, wd, gvec);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) v[e] = f2bf(args.mu * bf2f(v[e]) + bf2f(gv[e]));
-                IO::store(mbase, me.m_ld, r, col, h, wd, mvec, v);
+                    for (int e = 0; e < 8; ++e) v[e] = f2bf(args.mu * bf2f(v[e]) + bf2f(gv[e]));
+                    IO::store(mbase, me.m_ld, r, col, h, wd, mvec, v);
+                }
+                chunk[it] = v;
             }
-            chunk[it] = v;
         }
         float ss = 0.f;
 #pragma unroll
@@ -338,6 +348,24 @@ __global__ __launch_bounds__(512) void resident256_kernel(const ResidentArgs arg
         obase = reinterpret_cast<unsigned short*>(me.w) + (int64_t)tg.r0 * me.w_ld + tg.c0;
         old = me.w_ld;
         ovec = vec_ok(me.w, me.w_ld, tg.c0);
+    }
+    if (MUON && (tr ? (h == kT && wd == XR) : (h == XR && wd == kT)) && ovec) {
+        // the result's chunks from LDS, then W updated in batches
+        u16x8 x[NCH];
+#pragma unroll
+        for (int it = 0; it < NCH; ++it) {
+            const int idx = it * 512 + tid;
+            const int r = idx / cpr, col = (idx % cpr) * 8;
+            if (!tr) {
+                x[it] = *reinterpret_cast<const u16x8*>(&sX[r * kLD + col]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[it][e] = sX[(col + e) * kLD + r];
+            }
+        }
+        const int rpi = 512 / cpr;
+        muon_update_whole<NCH, 8>(obase + (int64_t)(tid / cpr) * old + (tid % cpr) * 8, (int64_t)rpi * old, args.eta, x);
+        return;
     }
 #pragma unroll
     for (int it = 0; it < NCH; ++it) {

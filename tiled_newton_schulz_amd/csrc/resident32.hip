@@ -171,6 +171,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(MUON ? 4 : 5
             const unsigned short* p0 = mbase + (int64_t)crow * me.m_ld + ccol;
             chunk[0] = *reinterpret_cast<const u16x8*>(p0);
             chunk[1] = *reinterpret_cast<const u16x8*>(p0 + 16 * me.m_ld);
+        } else if (MUON && full && vec_ok(me.g, me.g_ld, tg.c0)) {
+            const unsigned short* g0 = reinterpret_cast<const unsigned short*>(me.g) + (int64_t)tg.r0 * me.g_ld + tg.c0;
+            muon_prologue_whole<IO::NCH, IO::NCH>(mbase + (int64_t)crow * me.m_ld + ccol, 16 * me.m_ld,
+                                                  g0 + (int64_t)crow * me.g_ld + ccol, 16 * me.g_ld, args.mu, chunk);
         } else {
             const unsigned short* gbase = nullptr;
             bool gvec = false;
@@ -371,6 +375,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(MUON ? 4 : 5
                 old = me.w_ld;
                 ovec = vec_ok(me.w, me.w_ld, tg.c0);
             }
+            if (MUON && h == 32 && wd == 32 && ovec) {
+                muon_update_whole<IO::NCH, IO::NCH>(obase + (int64_t)crow * old + ccol, 16 * old, args.eta, out);
+            } else {
 #pragma unroll
             for (int it = 0; it < IO::NCH; ++it) {
                 const int r = crow + 16 * it;
@@ -381,6 +388,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(MUON ? 4 : 5
                     for (int e = 0; e < 8; ++e) v[e] = f2bf(bf2f(wv[e]) - args.eta * bf2f(v[e]));
                 }
                 IO::store(obase, old, r, ccol, h, wd, ovec, v);
+            }
             }
         }
         __syncthreads();
