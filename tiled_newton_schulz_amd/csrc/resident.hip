@@ -78,10 +78,10 @@ void resident_kernel(const ResidentArgs args) {
     using IO = TileIO<TK>;
     // Kernel tile 128 (plain map) is launched with at most one workgroup per
     // resident slot and walks its tiles with a grid stride.  The next tile is
-    // loaded into registers before the last step of the current one, and the
-    // stores of a tile drain while the next one starts, so that a wave's tile
-    // I/O overlaps MFMA work instead of every wave of a round loading (and
-    // storing) at the same time.
+    // loaded into registers, half before the last step of the current one and
+    // half before that step's X' product, and the stores of a tile drain while
+    // the next one starts, so that a wave's tile I/O overlaps MFMA work
+    // instead of every wave of a round loading (and storing) at the same time.
     constexpr bool PERSIST = TK == 128 && !MUON && !PRECISE;
     // Kernel tile 128 folds the normalisation into the first step (K > 0):
     // the raw tile goes to LDS, the sum of squares is the trace of the first
@@ -628,33 +628,51 @@ void resident_kernel(const ResidentArgs args) {
         __syncthreads();
     };
     auto no_hook = [](unsigned) {};
-    // The next tile's data, in flight during the last X' product and the
-    // stores, when it is a full aligned tile (ragged tiles are loaded at the
-    // top of their own iteration).  chunk is assigned on both paths, so that
+    // The next tile's data, in flight during the last step and the stores,
+    // when it is a full aligned tile (ragged tiles are loaded at the top of
+    // their own iteration).  chunk is assigned on both paths, so that
     // the previous tile's data is not kept live across the steps.
     bool pre = false;
-    auto prefetch = [&](unsigned after) {
-        if (next) {
-            const MatEntry& mn = args.mats[find_class(args.mats, args.nmats, tn)];
-            const TileGeom tgn = class_tile(mn, args.T, tn - mn.tile_base);
-            const unsigned short* nbase =
-                reinterpret_cast<const unsigned short*>(mn.m) + (int64_t)tgn.r0 * mn.m_ld + tgn.c0;
-            pre = tgn.h == TK && tgn.w == TK && vec_ok(mn.m, mn.m_ld, tgn.c0);
-            if (pre) {
+    // The prefetch comes in two parts: the first half of the chunks before
+    // the last step (part 0, which also finds the next tile), the second half
+    // before that step's X' product (part 1).  Loading all of them at either
+    // point was slower: early, the registers they hold crowd the last step;
+    // late, their loads are still in flight when the next tile starts.
+    const unsigned short* pf_p = nullptr;   // lane's first chunk of the next tile
+    int64_t pf_ld = 0;
+    auto prefetch_part = [&](int part, unsigned after) __attribute__((always_inline)) {
+        if (part == 0) {
+            pre = false;
+            if (next) {
+                const MatEntry& mn = args.mats[find_class(args.mats, args.nmats, tn)];
+                const TileGeom tgn = class_tile(mn, args.T, tn - mn.tile_base);
+                pre = tgn.h == TK && tgn.w == TK && vec_ok(mn.m, mn.m_ld, tgn.c0);
                 // chunk it of a lane: row RPI it + lane / CPR, columns 8 (lane % CPR) .. + 7
-                constexpr int RPI = 64 / IO::CPR;
-                int64_t off = (int64_t)(lane / IO::CPR) * mn.m_ld + (lane % IO::CPR) * 8;
-                asm volatile("" : "+v"(off) : "v"(after));
-                const unsigned short* p = nbase + off;
-#pragma unroll
-                for (int it = 0; it < IO::NCH; ++it)
-                    chunk[it] = *reinterpret_cast<const u16x8*>(p + (int64_t)(RPI * it) * mn.m_ld);
-                return;
+                pf_p = reinterpret_cast<const unsigned short*>(mn.m) + (int64_t)tgn.r0 * mn.m_ld + tgn.c0 +
+                       (int64_t)(lane / IO::CPR) * mn.m_ld + (lane % IO::CPR) * 8;
+                pf_ld = mn.m_ld;
             }
         }
+        constexpr int RPI = 64 / IO::CPR;
+        constexpr int HALF = IO::NCH / 2;
+        if (pre) {
+            const unsigned short* p = pf_p;
+            asm volatile("" : "+v"(p) : "v"(after));
 #pragma unroll
-        for (int it = 0; it < IO::NCH; ++it) chunk[it] = u16x8{};
+            for (int it = 0; it < HALF; ++it) {
+                const int c = part * HALF + it;
+                chunk[c] = *reinterpret_cast<const u16x8*>(p + (int64_t)(RPI * c) * pf_ld);
+            }
+        } else {
+#pragma unroll
+            for (int it = 0; it < HALF; ++it) chunk[part * HALF + it] = u16x8{};
+        }
     };
+    auto prefetch = [&](unsigned after) __attribute__((always_inline)) {
+        prefetch_part(0, after);
+        prefetch_part(1, after);
+    };
+    auto prefetch_rest = [&](unsigned after) __attribute__((always_inline)) { prefetch_part(1, after); };
     // a middle step, plain or in square form (the host never puts the first
     // or the last step in square form)
     auto mid_step = [&](int step) __attribute__((always_inline)) {
@@ -671,7 +689,8 @@ void resident_kernel(const ResidentArgs args) {
         if (args.K >= 2) {
             ns_step(0, no_hook, FIRSTC{}, std::false_type{});
             for (int step = 1; step < args.K - 1; ++step) mid_step(step);
-            ns_step(args.K - 1, prefetch, std::false_type{}, std::false_type{});
+            prefetch_part(0, 0u);
+            ns_step(args.K - 1, prefetch_rest, std::false_type{}, std::false_type{});
         } else if (args.K == 1) {
             ns_step(0, prefetch, FIRSTC{}, std::false_type{});
         } else {
