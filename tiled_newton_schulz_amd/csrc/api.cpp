@@ -474,6 +474,7 @@ void chunk_args(const std::vector<MatSpec>& specs, const Plan& plan, const Chunk
     a.wg_norm = std::min(kWgNormMax, std::max(1, c.sbmax));
     a.io_dtype = bf16_storage(dt) ? 0 : 1;
     a.wk_dtype = G.wk;
+    a.slab = step_slab_layout(a) ? 1 : 0;
     a.muon = muon ? 1 : 0;
     a.eps = eps;
     a.normalize = normalize ? 1 : 0;

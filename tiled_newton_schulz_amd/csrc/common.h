@@ -97,6 +97,8 @@ struct StepArgs {
     int32_t muon;
     float eps, mu, eta;
     int32_t normalize;          // 0: the tiles are used as they are (later runs of a tile-size schedule)
+    int32_t slab;               // 1: the bf16 workspace is laid out in column slabs (ws_off) for the
+                                // direct-to-LDS GEMMs; 0: row-major
     void* Xc;                   // oriented tiles, current step
     void* Xn;                   // oriented tiles, next step
     void* A;                    // Gram matrices A = X X^T
@@ -127,6 +129,21 @@ __host__ __device__ inline int find_class(const MatEntry* mats, int n, int t) {
 // tiles of a class follow one another, and so do their r x round8(r) Gram
 // buffers.
 __host__ __device__ inline int64_t round8(int64_t x) { return (x + 7) & ~int64_t(7); }
+
+// Element offset of (row, col) in an r-row workspace matrix of ld8-element
+// rows (ld8 a multiple of 8).  Row-major, or in slabs of 32 columns, each slab
+// holding its r row pieces one after another (the last slab is ld8 mod 32
+// wide when that is not 0).  A GEMM's k chunk of 32 columns over a run of rows
+// is then one contiguous range, whole 128-byte lines, where row-major rows of
+// a 512-wide tile give each row's 64-byte piece half a line (measured on
+// MI355X: T = 512 on the dense 8192 layer 9.9 -> 9.0 ms, identical results).
+// A 16-byte piece at a column that is a multiple of 8 never crosses a slab.
+__host__ __device__ inline int64_t ws_off(int64_t row, int64_t col, int64_t r, int64_t ld8, bool slab) {
+    if (!slab) return row * ld8 + col;
+    const int64_t c0 = col & ~int64_t(31);
+    const int64_t wd = ld8 - c0 < 32 ? ld8 - c0 : 32;
+    return c0 * r + row * wd + (col - c0);
+}
 
 struct TileGeom {
     int32_t r0, c0, h, w;   // position and size in the matrix
@@ -164,6 +181,9 @@ hipError_t launch_resident256(const ResidentArgs& a, bool muon, bool narrow, hip
 int resident_slots(int kernel_tile, bool muon, bool precise);   // tiles the device holds at once (0 on error)
 int device_cus();
 hipError_t launch_step_norm(const StepArgs& a, hipStream_t s);
+// Whether the step GEMMs of a chunk run the direct-to-LDS kernels (bf16
+// workspace addressed with 32-bit offsets): their workspace is in slabs.
+bool step_slab_layout(const StepArgs& a);
 hipError_t launch_step_gram(const StepArgs& a, hipStream_t s);
 hipError_t launch_step_poly(const StepArgs& a, hipStream_t s);
 hipError_t launch_step_apply(const StepArgs& a, hipStream_t s);

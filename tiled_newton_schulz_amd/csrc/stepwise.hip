@@ -213,7 +213,7 @@ __global__ __launch_bounds__(256) void step_norm_kernel(const StepArgs a) {
                 } else {
                     // row i of the tile, 8 elements; past w they are zero, so
                     // the row's padding up to round8(w) is written as zeros
-                    wstore8(xo + (int64_t)i * xld + j, v);
+                    wstore8(xo + ws_off(i, j, g.r, xld, a.slab != 0), v);
                 }
             }
         } else {
@@ -240,7 +240,7 @@ __global__ __launch_bounds__(256) void step_norm_kernel(const StepArgs a) {
 #pragma unroll
                     for (int e = 0; e < 8; ++e) v[e] = tileT[cc8 + e][j];
                     // 8 elements; past h they are zero (padding up to round8(h))
-                    wstore8(xo + (int64_t)(j0 + j) * xld + i0 + cc8, v);
+                    wstore8(xo + ws_off(j0 + j, i0 + cc8, g.r, xld, a.slab != 0), v);
                 }
             }
             __syncthreads();
@@ -280,8 +280,16 @@ __device__ __forceinline__ void store_out(const StepArgs& a, const MatEntry& me,
     }
 }
 
-// k chunk of the DMA GEMMs (elements)
+// k chunk of the DMA GEMMs (elements): one workspace slab
 constexpr int kAsyncBK = 32;
+
+// ws_off in the slab layout with 32-bit arithmetic: the direct-to-LDS GEMMs
+// run only where a tile's areas stay below 2 GiB
+__device__ __forceinline__ uint32_t slab_off(int row, int col, int r, int ld8) {
+    const int c0 = col & ~31;
+    const int wd = ld8 - c0 < 32 ? ld8 - c0 : 32;
+    return (uint32_t)c0 * (uint32_t)r + (uint32_t)(row * wd + (col - c0));
+}
 // Chunks whose largest tile has at least this many 128-row blocks run the
 // 256 x 256 block shape (measured on MI355X: the symmetric products gain from
 // r = 1024 on, 13 % at r = 2048 and 38 % for X X^T of an 8192 x 28672 matrix;
@@ -824,15 +832,15 @@ __global__ __launch_bounds__(AsyncShape<BIG>::NT) void step_gemm_async(const Ste
 #pragma unroll
         for (int j = 0; j < NPI; ++j) {
             const int pr = m0 + prow_j[j], pk = k0 + pcol_j[j];
-            const uint32_t po = (pr < prow && pk < kdim) ? ((uint32_t)pr * ldp + pk) * 2u : pbytes;
+            const uint32_t po = (pr < prow && pk < kdim) ? slab_off(pr, pk, prow, ldp) * 2u : pbytes;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rP, (LDS_AS void*)(dP + (wave * NPI + j) * 512), 16, po, 0, 0, 0);
             uint32_t qo;
             if (!NN) {
                 const int qr = n0 + qrow_j[j], qk = k0 + qcol_j[j];
-                qo = (qr < qrows && qk < kdim) ? ((uint32_t)qr * ldq + qk) * 2u : qbytes;
+                qo = (qr < qrows && qk < kdim) ? slab_off(qr, qk, qrows, ldq) * 2u : qbytes;
             } else {
                 const int qr = k0 + qrow_j[j], qc = n0 + qcol_j[j];
-                qo = (qr < kdim && qc < qcol) ? ((uint32_t)qr * ldq + qc) * 2u : qbytes;
+                qo = (qr < kdim && qc < qcol) ? slab_off(qr, qc, kdim, ldq) * 2u : qbytes;
             }
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rQ, (LDS_AS void*)(dQ + (wave * NPI + j) * 512), 16, qo, 0, 0, 0);
         }
@@ -1099,7 +1107,7 @@ __global__ __launch_bounds__(AsyncShape<BIG>::NT) void step_gemm_async(const Ste
             const int R = id / CH, ch = id % CH;
             const u32x4 v = *reinterpret_cast<const u32x4*>(&sbuf[sw(R, ch * 8)]);
             if (m0 + h * PR + R < rows_ok && n0 + ch * 8 < cols_ok && ch * 8 < cmax)
-                *reinterpret_cast<u32x4*>(Out + (int64_t)(m0 + h * PR + R) * ldo + n0 + ch * 8) = v;
+                *reinterpret_cast<u32x4*>(Out + slab_off(m0 + h * PR + R, n0 + ch * 8, rows_ok, ldo)) = v;
         }
         if (!SYM) continue;
         // mirror: transposed row c of this pass goes to row n0 + c, columns
@@ -1116,7 +1124,7 @@ __global__ __launch_bounds__(AsyncShape<BIG>::NT) void step_gemm_async(const Ste
             const int R = id >> 4, ch = id & 15;
             const u32x4 v = *reinterpret_cast<const u32x4*>(&sbuf[swt(R, ch * 8)]);
             if (R < tmax && n0 + R < rows_ok && m0 + h * PR + ch * 8 < cols_ok)
-                *reinterpret_cast<u32x4*>(Out + (int64_t)(n0 + R) * ldo + m0 + h * PR + ch * 8) = v;
+                *reinterpret_cast<u32x4*>(Out + slab_off(n0 + R, m0 + h * PR + ch * 8, rows_ok, ldo)) = v;
         }
     }
 }
@@ -1144,11 +1152,10 @@ hipError_t launch_step_norm(const StepArgs& a, hipStream_t s) {
 template <int MODE>
 static hipError_t launch_gemm(const StepArgs& a, hipStream_t s) {
     if (a.grid_blocks <= 0) return hipSuccess;
-    // the direct-to-LDS kernel addresses an operand with 32-bit byte offsets
-    const int64_t rmax = 128LL * a.nb_max, smax = 128LL * a.ns_max;
-    const bool small = rmax * std::max(rmax, smax) * 2 < (1LL << 31);
+    // the workspace layout (written by the normalisation pass) decides the kernel
+    const bool dma = a.slab != 0;
     const int big_nb = MODE == 2 ? kBigNbApply : kBigNbSym;
-    if (a.wk_dtype == 0 && small && a.nb_max >= big_nb) {
+    if (dma && a.nb_max >= big_nb) {
         // 256 x 256 blocks: the grid counts blocks of that size
         StepArgs b = a;
         const int64_t nt = a.tile_end - a.tile_begin;
@@ -1156,13 +1163,19 @@ static hipError_t launch_gemm(const StepArgs& a, hipStream_t s) {
         const int64_t bpt = MODE == 2 ? nbm * nsm : nbm * (nbm + 1) / 2;
         b.grid_blocks = (int32_t)((nt * bpt + 7) / 8 * 8);
         hipLaunchKernelGGL((step_gemm_async<MODE, true>), dim3(b.grid_blocks), dim3(512), 0, s, b);
-    } else if (a.wk_dtype == 0 && small)
+    } else if (dma)
         hipLaunchKernelGGL((step_gemm_async<MODE, false>), dim3(a.grid_blocks), dim3(256), 0, s, a);
     else if (a.wk_dtype == 0)
         hipLaunchKernelGGL((step_gemm_kernel<0, MODE>), dim3(a.grid_blocks), dim3(256), 0, s, a);
     else
         hipLaunchKernelGGL((step_gemm_kernel<1, MODE>), dim3(a.grid_blocks), dim3(256), 0, s, a);
     return hipGetLastError();
+}
+
+bool step_slab_layout(const StepArgs& a) {
+    // the direct-to-LDS kernel addresses an operand with 32-bit byte offsets
+    const int64_t rmax = 128LL * a.nb_max, smax = 128LL * a.ns_max;
+    return a.wk_dtype == 0 && rmax * std::max(rmax, smax) * 2 < (1LL << 31);
 }
 
 hipError_t launch_step_gram(const StepArgs& a, hipStream_t s) { return launch_gemm<0>(a, s); }
