@@ -13,6 +13,7 @@
 #include <vector>
 
 #include "common.h"
+#include "stepargs.h"
 #include "pair_stats.h"
 
 using namespace himuon;

@@ -77,40 +77,6 @@ struct Consts32 {
     int32_t neg;              // bit k: c_k < 0
 };
 
-// Arguments of the step-by-step path kernels for one chunk of tiles.
-struct StepArgs {
-    MatEntry mats[kGroup];
-    float abc[3 * kMaxSteps];
-    int32_t nmats;
-    int32_t T;
-    int32_t tile_begin;         // chunk = tiles [tile_begin, tile_end) of the group
-    int32_t tile_end;
-    int64_t xbase, abase;       // area offsets of tile_begin (subtracted from the class offsets)
-    int32_t step;               // Newton-Schulz step this launch runs
-    int32_t K;
-    int32_t nb_max;             // 128-row macro blocks along r of the largest tile
-    int32_t ns_max;             // 128-column macro blocks along s of the largest tile
-    int32_t wg_norm;            // workgroups per tile in the normalisation kernels
-    int32_t grid_blocks;        // workgroups launched (multiple of 8)
-    int32_t io_dtype;           // matrices: 0 bf16, 1 fp32
-    int32_t wk_dtype;           // workspace: 0 bf16, 1 fp32
-    int32_t muon;
-    float eps, mu, eta;
-    int32_t normalize;          // 0: the tiles are used as they are (later runs of a tile-size schedule)
-    int32_t slab;               // 1: the bf16 workspace is laid out in column slabs (ws_off) for the
-                                // direct-to-LDS GEMMs; 0: row-major
-    void* Xc;                   // oriented tiles, current step
-    void* Xn;                   // oriented tiles, next step
-    void* A;                    // Gram matrices A = X X^T
-    void* B;                    // B' = a I + b A + c A^2
-    float* partial;             // wg_norm partial sums of squares per tile
-    // product of two r x r matrices with a symmetric result, O = L M^T (Gram
-    // iteration); same layout and offsets as A
-    const void* L;
-    const void* M;
-    void* O;
-};
-
 // Index of the class holding tile t: the last entry with tile_base <= t
 // (binary search over the launch table; the search is uniform per wave).
 __host__ __device__ inline int find_class(const MatEntry* mats, int n, int t) {
@@ -129,21 +95,6 @@ __host__ __device__ inline int find_class(const MatEntry* mats, int n, int t) {
 // tiles of a class follow one another, and so do their r x round8(r) Gram
 // buffers.
 __host__ __device__ inline int64_t round8(int64_t x) { return (x + 7) & ~int64_t(7); }
-
-// Element offset of (row, col) in an r-row workspace matrix of ld8-element
-// rows (ld8 a multiple of 8).  Row-major, or in slabs of 32 columns, each slab
-// holding its r row pieces one after another (the last slab is ld8 mod 32
-// wide when that is not 0).  A GEMM's k chunk of 32 columns over a run of rows
-// is then one contiguous range, whole 128-byte lines, where row-major rows of
-// a 512-wide tile give each row's 64-byte piece half a line (measured on
-// MI355X: T = 512 on the dense 8192 layer 9.9 -> 9.0 ms, identical results).
-// A 16-byte piece at a column that is a multiple of 8 never crosses a slab.
-__host__ __device__ inline int64_t ws_off(int64_t row, int64_t col, int64_t r, int64_t ld8, bool slab) {
-    if (!slab) return row * ld8 + col;
-    const int64_t c0 = col & ~int64_t(31);
-    const int64_t wd = ld8 - c0 < 32 ? ld8 - c0 : 32;
-    return c0 * r + row * wd + (col - c0);
-}
 
 struct TileGeom {
     int32_t r0, c0, h, w;   // position and size in the matrix
@@ -180,14 +131,6 @@ Consts32 consts32(const float* abc, int K);
 hipError_t launch_resident256(const ResidentArgs& a, bool muon, bool narrow, hipStream_t s);
 int resident_slots(int kernel_tile, bool muon, bool precise);   // tiles the device holds at once (0 on error)
 int device_cus();
-hipError_t launch_step_norm(const StepArgs& a, hipStream_t s);
-// Whether the step GEMMs of a chunk run the direct-to-LDS kernels (bf16
-// workspace addressed with 32-bit offsets): their workspace is in slabs.
-bool step_slab_layout(const StepArgs& a);
-hipError_t launch_step_gram(const StepArgs& a, hipStream_t s);
-hipError_t launch_step_poly(const StepArgs& a, hipStream_t s);
-hipError_t launch_step_apply(const StepArgs& a, hipStream_t s);
-hipError_t launch_step_product(const StepArgs& a, hipStream_t s);
 // Device address of the library's scratch array on the current device
 // (static_scratch.hip); looked up once per device.
 hipError_t static_scratch(void** out);

@@ -23,6 +23,7 @@
 #include <algorithm>
 
 #include "device_util.h"
+#include "stepargs.h"
 
 namespace himuon {
 
