@@ -79,9 +79,9 @@ def run_gram(m):
 @pytest.mark.gpu
 @pytest.mark.parametrize("shape", [(1000, 1500), (2000, 2100), (2100, 1880)])
 def test_ragged_large_tiles_against_oracle(cuda, shape):
-    """r = 1000: the symmetric products run 256 x 256 blocks, apply 128 x 128;
-    r = 2000 and 1880: every product runs 256 x 256 blocks; none of the sides
-    is a multiple of 256."""
+    """r = 1000: every product runs 128 x 128 blocks; r = 2000 and 1880: every
+    product runs 256 x 256 blocks; none of the sides is a multiple of 256, so
+    each ends in a partial workspace slab of 32 columns."""
     x = workloads.round_to(np.random.default_rng([58, shape[0]]).standard_normal(shape), "bf16")
     xd = x.double().numpy()
     ref = oracle.full_matrix_ns(xd, MIXED)
@@ -103,7 +103,7 @@ def test_closed_form_long_k(cuda, shape, tall):
     """k >= 4096 walks blocks in groups of block rows: 4300 x 8600 (apply and
     the symmetric products, all 256 x 256 blocks, r = 4300 ragged), its
     transpose (worked on transposed), and 1000 x 5000 (X X^T with k = 5000,
-    grouped lower blocks)."""
+    grouped lower blocks of the 128 x 128 shape)."""
     Y, E = structured(shape[0], shape[1], seed=shape[0] + int(tall))
     if tall:
         Y, E = Y.T.copy(), E.T.copy()

@@ -292,11 +292,12 @@ __device__ __forceinline__ uint32_t slab_off(int row, int col, int r, int ld8) {
     return (uint32_t)c0 * (uint32_t)r + (uint32_t)(row * wd + (col - c0));
 }
 // Chunks whose largest tile has at least this many 128-row blocks run the
-// 256 x 256 block shape (measured on MI355X: the symmetric products gain from
-// r = 1024 on, 13 % at r = 2048 and 38 % for X X^T of an 8192 x 28672 matrix;
-// the apply product is level at r = s = 2048, 8 % faster at 2048 x 5632 and
-// 16 % at 8192 x 28672, and 6 % slower at r = s = 1024)
-constexpr int kBigNbSym = 8;
+// 256 x 256 block shape (measured on MI355X: the symmetric products are level
+// at r = 2048 and gain 38 % for X X^T of an 8192 x 28672 matrix; at r = 1024
+// the 128 x 128 shape is 3 % faster on the slab workspace (it was 13 % slower
+// on row-major rows); the apply product is level at r = s = 2048, 8 % faster
+// at 2048 x 5632 and 16 % at 8192 x 28672, and 6 % slower at r = s = 1024)
+constexpr int kBigNbSym = 16;
 constexpr int kBigNbApply = 16;
 template <int DT> struct GemmCfg;
 template <> struct GemmCfg<0> {
