@@ -853,7 +853,6 @@ __global__ __launch_bounds__(AsyncShape<BIG>::NT) void step_gemm_async(const Ste
     for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
-    unsigned avp[FM][FN][8];   // poly: A over the output block, bf16 pairs
 
     // symmetric products: both operands are row panels
     auto compute = [&](int kt, const ET* cP, const ET* cQ) __attribute__((always_inline)) {
@@ -877,26 +876,6 @@ __global__ __launch_bounds__(AsyncShape<BIG>::NT) void step_gemm_async(const Ste
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
-        }
-        if constexpr (MODE == 1) {
-            // A over this output block is the k range [n0 + wn 64 + j 32, +32)
-            // of the row panel (A symmetric): one k chunk
-#pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                const int c0 = n0 + wn * 64 + j * 32;
-                if (kt == c0 / BK) {
-                    const int cl = c0 - kt * BK + l32;
-#pragma unroll
-                    for (int i = 0; i < FM; ++i)
-#pragma unroll
-                        for (int q = 0; q < 16; ++q) {
-                            const int r = wm * WR + i * 32 + (q >> 2) * 8 + gl * 4 + (q & 3);
-                            const int pc = (cl >> 3) ^ ((r >> SH) & (CPR - 1));
-                            const unsigned v = cP[r * BK + pc * 8 + (cl & 7)];
-                            avp[i][j][q >> 1] = (q & 1) ? (avp[i][j][q >> 1] | (v << 16)) : v;
-                        }
-                }
-            }
         }
     };
 
@@ -964,6 +943,30 @@ __global__ __launch_bounds__(AsyncShape<BIG>::NT) void step_gemm_async(const Ste
     const float ca = a.abc[3 * a.step], cb = a.abc[3 * a.step + 1], cc = a.abc[3 * a.step + 2];
     auto sw = [](int row, int col) { return row * LDC + col; };
     auto swt = [](int row, int col) { return row * LDT + col; };
+    // poly: A over the output block, bf16 pairs in the MFMA's register order,
+    // read from the workspace once the products are done.  A is symmetric, so
+    // the lane's four consecutive rows of column c are the four consecutive
+    // elements of row c: one 8-byte load each.  (Taken from the row panel
+    // while its k chunk was in LDS, they held 32 registers through the loop,
+    // which left room for three workgroups per CU instead of four.)
+    unsigned avp[FM][FN][8];
+    if constexpr (MODE == 1) {
+        const ET* Ag = reinterpret_cast<const ET*>(a.A) + g.aoff;
+        const int ld8 = (int)round8(g.r);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const int col = n0 + wn * 64 + j * 32 + l32;
+                    const int row0 = m0 + wm * WR + i * 32 + m * 8 + gl * 4;
+                    u32x2 v = {0u, 0u};
+                    if (col < g.r && row0 < ld8) v = *reinterpret_cast<const u32x2*>(Ag + slab_off(col, row0, g.r, ld8));
+                    avp[i][j][2 * m] = v[0];
+                    avp[i][j][2 * m + 1] = v[1];
+                }
+    }
     // the result rounded to bf16, two rows a register: cvp[i][j][p] holds rows
     // 2p and 2p + 1 of the lane's 16 (the MFMA's register order)
     unsigned cvp[FM][FN][8];
