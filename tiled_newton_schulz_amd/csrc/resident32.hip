@@ -349,7 +349,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(MUON ? 4 : 5
         }
         // the last iterate in fp32 (Ym), times 1 / g in the square form,
         // rounded once
-        if (SQUARE && K > 0) Ym = Ym * cs.rlast;
+        // (the square form always has K >= 1: consts32 picks it only then, so
+        // no per-element select on K is needed here)
+        if constexpr (SQUARE) Ym = Ym * cs.rlast;
         if (SQUARE || K <= cs.n_master) {
             XR[0] = cvt8(Ym, 0);
             XR[1] = cvt8(Ym, 8);
