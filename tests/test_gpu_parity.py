@@ -120,6 +120,10 @@ def test_bf16_kernel_tile_256_shapes(cuda, T):
 
 @pytest.mark.parametrize("T", [160, 256, 512, 4096])
 def test_bf16_large_tile_shapes(cuda, T):
+    """bf16 tiles on the step path, whose workspace is laid out in 32-column
+    slabs: padded row lengths of 304, 136, 264, 520 and 600/704 leave a last
+    slab of 16, 8 or 24 columns (or none), tall tiles (600 x 130) are stored
+    transposed, and T = 160 / 256 put the same shapes on chip for contrast."""
     rng = np.random.default_rng([12, T])
     for (h, w) in [(300, 299), (129, 600), (600, 130), (513, 257), (700, 520)]:
         x = workloads.round_to(rng.standard_normal((h, w)), "bf16")
