@@ -538,6 +538,9 @@ himuon_status_t run(const std::vector<MatSpec>& specs, int32_t T, int32_t K, con
         const int64_t nt = c.te - c.tb;
         hipError_t e = launch_step_norm(a, s);
         if (e != hipSuccess) return hip_fail(e);
+        // the pass wrote the tiles unscaled: the first Gram and apply products
+        // take each tile's scale in their epilogue
+        a.x_raw = 1;
         for (int step = 0; step < K; ++step) {
             a.step = step;
             const int64_t tri = (int64_t)a.nb_max * (a.nb_max + 1) / 2;
@@ -546,6 +549,7 @@ himuon_status_t run(const std::vector<MatSpec>& specs, int32_t T, int32_t K, con
             if ((e = launch_step_poly(a, s)) != hipSuccess) return hip_fail(e);
             a.grid_blocks = (int32_t)(((nt * a.nb_max * a.ns_max) + 7) / 8 * 8);
             if ((e = launch_step_apply(a, s)) != hipSuccess) return hip_fail(e);
+            a.x_raw = 0;
             std::swap(a.Xc, a.Xn);
         }
     }
@@ -612,10 +616,14 @@ himuon_status_t run_gram(const std::vector<MatSpec>& specs, int32_t T, int32_t K
             a.step = step;
             a.grid_blocks = apply_grid;
             hipError_t e = launch_step_apply(a, s);
+            a.x_raw = 0;   // X now holds the scaled product
             std::swap(a.Xc, a.Xn);
             return e;
         };
         hipError_t e = launch_step_norm(a, s);
+        // the pass wrote the tiles unscaled (K >= 1): the first X X^T and the
+        // first apply of Q take each tile's scale in their epilogue
+        a.x_raw = K > 0 ? 1 : 0;
         if (e == hipSuccess) e = gram_of_x();
         void* Q = nullptr;   // nullptr: the identity
         for (int32_t t = 1; t <= K && e == hipSuccess; ++t) {

@@ -29,6 +29,9 @@ struct StepArgs {
     int32_t normalize;          // 0: the tiles are used as they are (later runs of a tile-size schedule)
     int32_t slab;               // 1: the bf16 workspace is laid out in column slabs (ws_off) for the
                                 // direct-to-LDS GEMMs; 0: row-major
+    int32_t x_raw;              // 1: X holds the tiles as loaded, not yet scaled; the Gram product and
+                                // the apply product that read it scale their result by the tile's
+                                // 1 / (|X|_F + eps) (squared for X X^T), from the partial sums
     void* Xc;                   // oriented tiles, current step
     void* Xn;                   // oriented tiles, next step
     void* A;                    // Gram matrices A = X X^T
@@ -56,6 +59,9 @@ __host__ __device__ inline int64_t ws_off(int64_t row, int64_t col, int64_t r, i
     return c0 * r + row * wd + (col - c0);
 }
 
+// K >= 1: one pass that takes the partial sums of squares and writes the
+// oriented tiles unscaled (the caller then sets x_raw for the first Gram and
+// apply products); K = 0: the sums, then the normalised tiles in place.
 hipError_t launch_step_norm(const StepArgs& a, hipStream_t s);
 // Whether the step GEMMs of a chunk run the direct-to-LDS kernels (bf16
 // workspace addressed with 32-bit offsets): their workspace is in slabs.

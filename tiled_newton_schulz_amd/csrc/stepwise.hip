@@ -58,6 +58,14 @@ __device__ __forceinline__ TileRef find_tile(const StepArgs& a, int t) {
     return r;
 }
 
+// Scale of chunk tile tl, 1 / (|X|_F + eps), from the normalisation pass's
+// partial sums (summed in the same order wherever it is taken)
+__device__ __forceinline__ float tile_scale(const StepArgs& a, int tl) {
+    float tot = 0.f;
+    for (int i = 0; i < a.wg_norm; ++i) tot += a.partial[(int64_t)tl * a.wg_norm + i];
+    return a.normalize ? 1.0f / (sqrtf(tot) + a.eps) : 1.0f;
+}
+
 __device__ __forceinline__ float block_sum(float v, float* red) {
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
@@ -150,16 +158,23 @@ __global__ __launch_bounds__(256) void step_norm_kernel(const StepArgs a) {
         }
     };
 
-    if (PASS == 0) {
+    if (PASS == 0 || PASS == 2) {
+        // sums of squares of this workgroup's 64 x 64 sub-blocks (Muon: of the
+        // new momentum, stored); PASS 2 also writes the oriented tile unscaled
         const ET* gbase = a.muon ? reinterpret_cast<const ET*>(me.g) + (int64_t)g.r0 * me.g_ld + g.c0 : nullptr;
+        WT* xo = reinterpret_cast<WT*>(a.Xc) + g.xoff;
+        const int64_t xld = round8(g.s);
         float ss = 0.f;
         for (int sb = k; sb < sbw * sbh; sb += a.wg_norm) {
             const int i0 = (sb / sbw) * 64, j0 = (sb % sbw) * 64;
+            float vk[2][8];   // the two runs of 8 this thread holds (zero outside the tile)
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
                 const int i = i0 + rr + 32 * half, j = j0 + cc8;
+                float (&v)[8] = vk[half];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] = 0.f;
                 if (i >= g.h || j >= g.w) continue;
-                float v[8];
                 load8(mbase, me.m_ld, i, j, g.w, v);
                 if (a.muon) {
                     float gv[8];
@@ -173,6 +188,30 @@ __global__ __launch_bounds__(256) void step_norm_kernel(const StepArgs a) {
                 }
 #pragma unroll
                 for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(v[e], v[e], ss);
+                // row i of the tile, 8 elements; past w they are zero, so the
+                // row's padding up to round8(w) is written as zeros
+                if (PASS == 2 && !g.tr) wstore8(xo + ws_off(i, j, g.r, xld, a.slab != 0), v);
+            }
+            if (PASS == 2 && g.tr) {
+                // tall tile: stored transposed, through LDS so both sides move
+                // whole runs
+#pragma unroll
+                for (int half = 0; half < 2; ++half)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) tileT[rr + 32 * half][cc8 + e] = vk[half][e];
+                __syncthreads();
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    const int j = rr + 32 * half;   // oriented row (original column j0 + j)
+                    if (j0 + j < g.w && i0 + cc8 < g.h) {
+                        float v[8];
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) v[e] = tileT[cc8 + e][j];
+                        // 8 elements; past h they are zero (padding up to round8(h))
+                        wstore8(xo + ws_off(j0 + j, i0 + cc8, g.r, xld, a.slab != 0), v);
+                    }
+                }
+                __syncthreads();
             }
         }
         ss = block_sum(ss, red);
@@ -180,9 +219,7 @@ __global__ __launch_bounds__(256) void step_norm_kernel(const StepArgs a) {
         return;
     }
 
-    float tot = 0.f;
-    for (int i = 0; i < a.wg_norm; ++i) tot += a.partial[(int64_t)tl * a.wg_norm + i];
-    const float scale = a.normalize ? 1.0f / (sqrtf(tot) + a.eps) : 1.0f;
+    const float scale = tile_scale(a, tl);
     WT* xo = reinterpret_cast<WT*>(a.Xc) + g.xoff;
     const int64_t xld = round8(g.s);
     ET* wbase = a.muon ? reinterpret_cast<ET*>(me.w) + (int64_t)g.r0 * me.w_ld + g.c0 : nullptr;
@@ -318,7 +355,7 @@ template <> struct GemmCfg<1> {
 template <int DT, int MODE>
 __device__ __forceinline__ void gemm_epilogue(const StepArgs& a, const TileRef& tref, int bm, int bn, int m0,
                                               int n0, int wm, int wn, int l32, int gl, const f32x16 (&acc)[2][2],
-                                              const float (&aval)[2][2][16]) {
+                                              const float (&aval)[2][2][16], float xs) {
     using E = Elem<DT>;
     using ET = typename E::T;
     const TileGeom& g = tref.g;
@@ -335,7 +372,12 @@ __device__ __forceinline__ void gemm_epilogue(const StepArgs& a, const TileRef& 
                 const int col = n0 + wn * 64 + j * 32 + l32;
                 float v[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * m + e];
+                for (int e = 0; e < 4; ++e) {
+                    v[e] = acc[i][j][4 * m + e];
+                    // X read unscaled: X X^T takes the scale twice, B' X once
+                    if (MODE == 0) v[e] = (v[e] * xs) * xs;
+                    if (MODE == 2) v[e] *= xs;
+                }
                 if (MODE != 2) {
                     // columns up to the padded row length are written: past r
                     // the product is exactly zero (zero operand rows), which
@@ -650,7 +692,8 @@ __global__ __launch_bounds__(256) void step_gemm_kernel(const StepArgs a) {
         __syncthreads();
     }
 
-    gemm_epilogue<DT, MODE>(a, tref, bm, bn, m0, n0, wm, wn, l32, gl, acc, aval);
+    const float xs = ((MODE == 0 || MODE == 2) && a.x_raw) ? tile_scale(a, tl) : 1.0f;
+    gemm_epilogue<DT, MODE>(a, tref, bm, bn, m0, n0, wm, wn, l32, gl, acc, aval, xs);
 }
 
 // ---------------------------------------------------------------------------
@@ -967,6 +1010,9 @@ __global__ __launch_bounds__(AsyncShape<BIG>::NT) void step_gemm_async(const Ste
                     avp[i][j][2 * m + 1] = v[1];
                 }
     }
+    // X read unscaled (the first Gram and apply products after the
+    // normalisation pass): X X^T takes the tile's scale twice, B' X once
+    const float xs = ((MODE == 0 || MODE == 2) && a.x_raw) ? tile_scale(a, tl) : 1.0f;
     // the result rounded to bf16, two rows a register: cvp[i][j][p] holds rows
     // 2p and 2p + 1 of the lane's 16 (the MFMA's register order)
     unsigned cvp[FM][FN][8];
@@ -977,6 +1023,8 @@ __global__ __launch_bounds__(AsyncShape<BIG>::NT) void step_gemm_async(const Ste
 #pragma unroll
             for (int q = 0; q < 16; ++q) {
                 float v = acc[i][j][q];
+                if constexpr (MODE == 0) v = (v * xs) * xs;
+                if constexpr (MODE == 2) v *= xs;
                 if constexpr (MODE == 1) {
                     const float av = (q & 1) ? hi_f(avp[i][j][q >> 1]) : lo_f(avp[i][j][q >> 1]);
                     v = __builtin_fmaf(cc, v, cb * av);
@@ -1149,6 +1197,7 @@ static hipError_t launch_norm_pass(const StepArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_step_norm(const StepArgs& a, hipStream_t s) {
+    if (a.K > 0) return launch_norm_pass<2>(a, s);
     hipError_t e = launch_norm_pass<0>(a, s);
     if (e != hipSuccess) return e;
     return launch_norm_pass<1>(a, s);
