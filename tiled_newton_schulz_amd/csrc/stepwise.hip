@@ -872,6 +872,10 @@ __global__ __launch_bounds__(AsyncShape<BIG>::NT) void step_gemm_async(const Ste
             qcol_j[j] = sub * 128 + ((pp & 15) ^ ((rn & 3) * 4)) * 8;
         }
     }
+    // a diagonal block of X X^T or A A has the same row panel as both operands:
+    // it is loaded once (at r = 512, 4 of the 10 lower blocks, a fifth of the
+    // launch's loads from L2 into LDS)
+    const bool one_panel = (MODE == 0 || MODE == 1) && bm == bn;
     auto issue = [&](int kt, ET* dP, ET* dQ) __attribute__((always_inline)) {
         const int k0 = kt * BK;
 #pragma unroll
@@ -887,7 +891,8 @@ __global__ __launch_bounds__(AsyncShape<BIG>::NT) void step_gemm_async(const Ste
                 const int qr = k0 + qrow_j[j], qc = n0 + qcol_j[j];
                 qo = (qr < kdim && qc < qcol) ? slab_off(qr, qc, kdim, ldq) * 2u : qbytes;
             }
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rQ, (LDS_AS void*)(dQ + (wave * NPI + j) * 512), 16, qo, 0, 0, 0);
+            if (!one_panel)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rQ, (LDS_AS void*)(dQ + (wave * NPI + j) * 512), 16, qo, 0, 0, 0);
         }
     };
 
@@ -973,7 +978,8 @@ __global__ __launch_bounds__(AsyncShape<BIG>::NT) void step_gemm_async(const Ste
                         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[kk][i], bv[kk][j], acc[i][j], 0, 0, 0);
         } else {
             if (kt + 1 < nk) issue(kt + 1, cur ? sP0 : sP1, cur ? sQ0 : sQ1);
-            compute(kt, cur ? sP1 : sP0, cur ? sQ1 : sQ0);
+            const ET* cP = cur ? sP1 : sP0;
+            compute(kt, cP, one_panel ? cP : (cur ? sQ1 : sQ0));
         }
     }
 
