@@ -385,6 +385,46 @@ def check_muon(W, M, G, Wg, Mg, dt, T, K, mu, eta, tiles=None):
     return worst
 
 
+@pytest.mark.parametrize("K", [0, 1, 2])
+@pytest.mark.parametrize("dt", ["bf16", "fp32", "bf16_precise"])
+def test_step_path_short_runs(cuda, dt, K):
+    """The step path with K = 0, 1 and 2.  The normalisation pass writes the
+    tiles unscaled and the first Gram and apply products apply each tile's
+    scale; with K = 1 both happen in the last step, whose apply writes the
+    result in place (a tall matrix's tiles transposed back).  T = 512 (tiles
+    with ragged edges) and T = 1024 (one tile per matrix), wide and tall;
+    bf16_precise is bf16 storage on the fp32 workspace."""
+    rng = np.random.default_rng([61, K, len(dt)])
+    io = "fp32" if dt == "fp32" else "bf16"
+    for (h, w) in [(700, 520), (520, 700)]:
+        x = workloads.round_to(rng.standard_normal((h, w)) * 3.0, io)
+        for T in (512, 1024):
+            g = x.cuda()
+            H.himuon_tiled_ns([g], T, K, MIXED[:K] if K else [], precise=(dt == "bf16_precise"))
+            torch.cuda.synchronize()
+            ref = oracle.tiled_ns(x.double().numpy(), T, MIXED[:K] if K else [], K=K)
+            err = float(oracle.tile_rel_errors(to_np(g), ref, T).max())
+            say(f"{dt} {h}x{w} T={T} K={K}: {err:.3e}")
+            assert err <= TOL["fp32" if dt == "fp32" else "bf16"], (h, w, T, err)
+
+
+@pytest.mark.parametrize("K", [1, 2])
+def test_muon_step_on_step_path_short_runs(cuda, K):
+    """The fused Muon step on the step path with K = 1 and 2: the momentum is
+    written unscaled by the normalisation pass, and with K = 1 the first
+    apply is also the one that writes W <- W - eta X."""
+    rng = np.random.default_rng([62, K])
+    shape = (700, 1100)
+    W, M, G = (workloads.round_to(rng.standard_normal(shape), "bf16") for _ in range(3))
+    Wg, Mg, Gg = W.cuda(), M.cuda(), G.cuda()
+    mu, eta = 0.95, 0.02
+    H.himuon_muon_step([Wg], [Mg], [Gg], 512, K, COEFFS, mu=mu, eta=eta)
+    torch.cuda.synchronize()
+    worst = check_muon(W, M, G, Wg, Mg, "bf16", 512, K, mu, eta)
+    say(f"muon bf16 {shape} T=512 K={K}: worst difference / bound = {worst:.3f}")
+    assert worst <= 1.0
+
+
 @pytest.mark.parametrize("shape,T", [((1100, 1030), 512), ((2100, 2100), 2100), ((1030, 2100), 2100)])
 def test_muon_step_on_step_path(cuda, shape, T):
     """The fused Muon step where the last product writes W <- W - eta X from
