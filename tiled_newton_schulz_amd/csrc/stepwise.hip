@@ -9,9 +9,11 @@
 //   poly : B' = a I + b A + c A A lower blocks (A symmetric, so A A = A A^T)
 //   apply: X' = B' X             (equal to a X + B X in exact arithmetic)
 // The last apply writes the result in place in the input dtype, undoing the
-// orientation.  Two small launches before the steps take the per-tile sum of
+// orientation.  One launch before the steps takes the per-tile partial sums of
 // squares (fixed partition and order, so the result is deterministic) and
-// write the normalised, oriented tiles.
+// writes the oriented tiles unscaled; the first gram and apply launches scale
+// their results by the tile's 1 / (||X||_F + eps) (twice for X X^T), so the
+// tiles are read once and the first products see them unrounded.
 //
 // bf16 workspaces use step_gemm_async (global -> LDS by buffer_load ... lds,
 // epilogue through LDS); fp32 workspaces and operands of 2 GiB or more use
@@ -83,9 +85,11 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
 // ---------------------------------------------------------------------------
 // Normalisation.  Grid: wg_norm workgroups per tile; workgroup k of a tile
 // handles the tile's 64x64 sub-blocks k, k + wg_norm, ...
-// Pass 0 (partial): Muon prologue M <- mu M + G (stored), partial sum of squares.
-// Pass 1 (write): scale = 1 / (sqrt(sum of the tile's partials) + eps); write
-// the scaled tile oriented into Xc, or, when K == 0, straight back in place.
+// Pass 2 (K >= 1): Muon prologue M <- mu M + G (stored), partial sum of
+// squares, and the tile written oriented and unscaled into Xc.
+// K == 0: pass 0 (the prologue and the partial sums), then pass 1: scale =
+// 1 / (sqrt(sum of the tile's partials) + eps) and the scaled tile written
+// straight back in place (Muon: W <- W - eta X).
 // ---------------------------------------------------------------------------
 template <int IO, int WK, int PASS>
 __global__ __launch_bounds__(256) void step_norm_kernel(const StepArgs a) {
@@ -219,69 +223,31 @@ __global__ __launch_bounds__(256) void step_norm_kernel(const StepArgs a) {
         return;
     }
 
+    // pass 1 (K == 0): the normalised tile, in place (Muon: W -= eta * it)
     const float scale = tile_scale(a, tl);
-    WT* xo = reinterpret_cast<WT*>(a.Xc) + g.xoff;
-    const int64_t xld = round8(g.s);
     ET* wbase = a.muon ? reinterpret_cast<ET*>(me.w) + (int64_t)g.r0 * me.w_ld + g.c0 : nullptr;
     for (int sb = k; sb < sbw * sbh; sb += a.wg_norm) {
         const int i0 = (sb / sbw) * 64, j0 = (sb % sbw) * 64;
-        if (a.K == 0 || !g.tr) {
 #pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                const int i = i0 + rr + 32 * half, j = j0 + cc8;
-                if (i >= g.h || j >= g.w) continue;
-                float v[8];
-                load8(mbase, me.m_ld, i, j, g.w, v);
+        for (int half = 0; half < 2; ++half) {
+            const int i = i0 + rr + 32 * half, j = j0 + cc8;
+            if (i >= g.h || j >= g.w) continue;
+            float v[8];
+            load8(mbase, me.m_ld, i, j, g.w, v);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) v[e] *= scale;
-                if (a.K == 0) {
-                    // output = normalised tile, in place (Muon: W -= eta * it)
-                    if (a.muon) {
-                        float wv[8];
-                        load8(wbase, me.w_ld, i, j, g.w, wv);
+            for (int e = 0; e < 8; ++e) v[e] *= scale;
+            if (a.muon) {
+                float wv[8];
+                load8(wbase, me.w_ld, i, j, g.w, wv);
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) {
-                            const ET r = E::cv(v[e]);
-                            wv[e] = wv[e] - a.eta * E::ld(&r);
-                        }
-                        store8(wbase, me.w_ld, i, j, g.w, wv);
-                    } else {
-                        store8(mbase, me.m_ld, i, j, g.w, v);
-                    }
-                } else {
-                    // row i of the tile, 8 elements; past w they are zero, so
-                    // the row's padding up to round8(w) is written as zeros
-                    wstore8(xo + ws_off(i, j, g.r, xld, a.slab != 0), v);
+                for (int e = 0; e < 8; ++e) {
+                    const ET r = E::cv(v[e]);
+                    wv[e] = wv[e] - a.eta * E::ld(&r);
                 }
+                store8(wbase, me.w_ld, i, j, g.w, wv);
+            } else {
+                store8(mbase, me.m_ld, i, j, g.w, v);
             }
-        } else {
-            // tall tile: stored transposed, through LDS so both sides move whole runs
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                const int i = rr + 32 * half;
-                float v[8];
-                if (i0 + i < g.h && j0 + cc8 < g.w) {
-                    load8(mbase, me.m_ld, i0 + i, j0 + cc8, g.w, v);
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) v[e] = 0.f;
-                }
-#pragma unroll
-                for (int e = 0; e < 8; ++e) tileT[i][cc8 + e] = v[e] * scale;
-            }
-            __syncthreads();
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                const int j = rr + 32 * half;        // oriented row (original column j0 + j)
-                if (j0 + j < g.w && i0 + cc8 < g.h) {
-                    float v[8];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) v[e] = tileT[cc8 + e][j];
-                    // 8 elements; past h they are zero (padding up to round8(h))
-                    wstore8(xo + ws_off(j0 + j, i0 + cc8, g.r, xld, a.slab != 0), v);
-                }
-            }
-            __syncthreads();
         }
     }
 }
