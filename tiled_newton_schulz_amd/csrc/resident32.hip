@@ -154,11 +154,19 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(MUON ? 4 : 5
         const int o = base + (p | 15) < n ? ((p & ~15) | ((p & 7) << 1) | ((p >> 3) & 1)) : p;
         return args.tile_begin + base + o;
     };
+    // class of the previous tile and its tile range: consecutive tiles of a
+    // wave mostly fall in the same class, which then needs no search
+    int cls = 0, cls_lo = 1, cls_hi = 0;
     for (int base = 0; base < n; base += gridDim.x) {
         if (base + p >= n) break;
         const int t = tile_at(base);
+        if (t < cls_lo || t >= cls_hi) {
+            cls = find_class(args.mats, args.nmats, t);
+            cls_lo = args.mats[cls].tile_base;
+            cls_hi = cls + 1 < args.nmats ? args.mats[cls + 1].tile_base : 0x7fffffff;
+        }
 
-        const MatEntry& me = args.mats[find_class(args.mats, args.nmats, t)];
+        const MatEntry& me = args.mats[cls];
         const TileGeom tg = class_tile(me, args.T, t - me.tile_base);
         const int h = tg.h, wd = tg.w;
         unsigned short* mbase = reinterpret_cast<unsigned short*>(me.m) + (int64_t)tg.r0 * me.m_ld + tg.c0;
