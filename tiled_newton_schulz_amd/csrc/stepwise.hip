@@ -492,6 +492,9 @@ __global__ __launch_bounds__(256) void step_gemm_kernel(const StepArgs a) {
     constexpr int NCP = 128 * BK / EPC / 256;
     static_assert(NCP * 256 * EPC == 128 * BK, "panel chunks must cover the panel");
     u32x4 rp[NCP], rq[NCP];
+    // a diagonal block of X X^T or A A has the same row panel as both operands:
+    // it is loaded and stored once
+    const bool one_panel = (MODE == 0 || MODE == 1) && bm == bn;
     auto load_panels = [&](int k0) {
 #pragma unroll
         for (int p = 0; p < NCP; ++p) {
@@ -510,7 +513,7 @@ __global__ __launch_bounds__(256) void step_gemm_kernel(const StepArgs a) {
                 }
                 rp[p] = v;
             }
-            if (!NN) {
+            if (!NN && !one_panel) {
                 const int row = c / (BK / EPC), kc = (c % (BK / EPC)) * EPC;
                 u32x4 v = {0, 0, 0, 0};
                 const int gr = n0 + row, gk = k0 + kc;
@@ -554,7 +557,9 @@ __global__ __launch_bounds__(256) void step_gemm_kernel(const StepArgs a) {
                 for (int q = 0; q < 4; ++q) reinterpret_cast<unsigned*>(sP)[row * LDP + kc + q] = rp[p][q];
             }
             if (!NN) {
-                if (DT == 0) {
+                if (one_panel) {
+                    // compute reads the P stage for both operands
+                } else if (DT == 0) {
                     *reinterpret_cast<u32x4*>(&sQ[row * LDP + kc]) = rq[p];
                 } else {
 #pragma unroll
@@ -576,7 +581,7 @@ __global__ __launch_bounds__(256) void step_gemm_kernel(const StepArgs a) {
 
     auto compute = [&](int stage) {
         const ET* sP = sP2 + stage * PSZ;
-        const ET* sQ = sQ2 + stage * QSZ;
+        const ET* sQ = one_panel ? sP : sQ2 + stage * QSZ;
         if constexpr (DT == 0) {
 #pragma unroll
             for (int kk = 0; kk < BK / 16; ++kk) {
